@@ -1,0 +1,167 @@
+// C ABI of liblynx: argument validation, workspace layout and dispatch.
+// The operations themselves are defined in lynx.h; the kernels live in the
+// other translation units.
+#include <atomic>
+#include <cstring>
+
+#include "lynx_internal.h"
+
+namespace lynx {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+constexpr int64_t kMaxElems = int64_t(1) << 31;
+
+inline size_t round_up256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool rank_ok(int64_t R) { return R == 0 || R == 16 || R == 32 || R == 48 || R == 64; }
+
+bool dims_ok(int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || N < 0 || K <= 0) return false;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
+    if (K % 128 != 0) return false;
+    if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return false;
+    return true;
+}
+
+struct WorkspaceLayout {
+    size_t values, meta, scale, T, total;
+};
+
+WorkspaceLayout layout_for(int64_t M, int64_t K, int64_t R) {
+    WorkspaceLayout L;
+    L.values = 0;
+    L.meta = L.values + round_up256(size_t(M) * size_t(K / 2) * 2);
+    L.scale = L.meta + round_up256(size_t(M) * size_t(K / 8));
+    L.T = L.scale + round_up256(size_t(M) * 4);
+    L.total = L.T + round_up256(size_t(M) * size_t(R) * 2);
+    return L;
+}
+}  // namespace
+
+lynx_status check_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LYNX_ERR_UNSUPPORTED_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return LYNX_ERR_UNSUPPORTED_DEVICE;
+    int st = g_arch_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return LYNX_ERR_DEVICE;
+        }
+        st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? LYNX_OK : LYNX_ERR_UNSUPPORTED_DEVICE;
+}
+
+}  // namespace lynx
+
+using namespace lynx;
+
+extern "C" {
+
+const char* lynx_status_string(lynx_status s) {
+    switch (s) {
+        case LYNX_OK: return "LYNX_OK";
+        case LYNX_ERR_NULL: return "LYNX_ERR_NULL: a required pointer is NULL";
+        case LYNX_ERR_SHAPE: return "LYNX_ERR_SHAPE: a size is outside the supported limits";
+        case LYNX_ERR_ALIGN: return "LYNX_ERR_ALIGN: a pointer is not 16-byte aligned";
+        case LYNX_ERR_WORKSPACE: return "LYNX_ERR_WORKSPACE: workspace is NULL or too small";
+        case LYNX_ERR_DEVICE: return "LYNX_ERR_DEVICE: a HIP call or kernel launch failed";
+        case LYNX_ERR_UNSUPPORTED_DEVICE:
+            return "LYNX_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950";
+    }
+    return "LYNX_ERR_UNKNOWN";
+}
+
+int lynx_version(void) { return 100; }
+
+size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+    if (!dims_ok(M, 1, K) || !rank_ok(R)) return 0;
+    return layout_for(M, K, R).total;
+}
+
+lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB, int64_t M, int64_t K, int64_t R,
+                          uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,
+                          lynx_stream_t stream) {
+    if (!dims_ok(M, 1, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
+    if (M == 0) return LYNX_OK;
+    if (!X || !values || !meta || !scale) return LYNX_ERR_NULL;
+    if (R > 0 && (!LB || !T)) return LYNX_ERR_NULL;
+    if (!aligned16(X) || !aligned16(values) || !aligned16(meta) || !aligned16(scale))
+        return LYNX_ERR_ALIGN;
+    if (R > 0 && (!aligned16(LB) || !aligned16(T))) return LYNX_ERR_ALIGN;
+    lynx_status st = check_device();
+    if (st != LYNX_OK) return st;
+    return launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values, meta, scale,
+                           R > 0 ? T : nullptr, static_cast<hipStream_t>(stream));
+}
+
+lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t* meta,
+                                           const float* scale, const uint16_t* T,
+                                           const uint16_t* W, const uint16_t* LA, uint16_t* Y,
+                                           int64_t M, int64_t N, int64_t K, int64_t R,
+                                           lynx_stream_t stream) {
+    if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
+    if (M == 0 || N == 0) return LYNX_OK;
+    if (!values || !meta || !scale || !W || !Y) return LYNX_ERR_NULL;
+    if (R > 0 && (!T || !LA)) return LYNX_ERR_NULL;
+    if (!aligned16(values) || !aligned16(meta) || !aligned16(scale) || !aligned16(W) ||
+        !aligned16(Y))
+        return LYNX_ERR_ALIGN;
+    if (R > 0 && (!aligned16(T) || !aligned16(LA))) return LYNX_ERR_ALIGN;
+    lynx_status st = check_device();
+    if (st != LYNX_OK) return st;
+    return launch_gemm_sparse(values, meta, scale, R > 0 ? T : nullptr, W, R > 0 ? LA : nullptr,
+                              Y, int(M), int(N), int(K), int(R),
+                              static_cast<hipStream_t>(stream));
+}
+
+lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                                    const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N,
+                                    int64_t K, int64_t R, void* workspace,
+                                    size_t workspace_bytes, lynx_stream_t stream) {
+    if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
+    if (M == 0 || N == 0) return LYNX_OK;
+    if (!X || !W || !Y) return LYNX_ERR_NULL;
+    if (R > 0 && (!LA || !LB)) return LYNX_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
+    if (R > 0 && (!aligned16(LA) || !aligned16(LB))) return LYNX_ERR_ALIGN;
+    const WorkspaceLayout L = layout_for(M, K, R);
+    if (!workspace || workspace_bytes < L.total) return LYNX_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LYNX_ERR_ALIGN;
+    lynx_status st = check_device();
+    if (st != LYNX_OK) return st;
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* values = reinterpret_cast<uint16_t*>(ws + L.values);
+    uint8_t* meta = reinterpret_cast<uint8_t*>(ws + L.meta);
+    float* scale = reinterpret_cast<float*>(ws + L.scale);
+    uint16_t* T = R > 0 ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values, meta, scale, T,
+                         s);
+    if (st != LYNX_OK) return st;
+    return launch_gemm_sparse(values, meta, scale, T, W, R > 0 ? LA : nullptr, Y, int(M), int(N),
+                              int(K), int(R), s);
+}
+
+lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
+                              int64_t N, int64_t K, lynx_stream_t stream) {
+    if (!dims_ok(M, N, K)) return LYNX_ERR_SHAPE;
+    if (M == 0 || N == 0) return LYNX_OK;
+    if (!X || !W || !Y) return LYNX_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
+    lynx_status st = check_device();
+    if (st != LYNX_OK) return st;
+    return launch_gemm_dense(X, W, Y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+"""Benchmark of the RT-Lynx sparse + LoRA linear layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload mlp_up] [--no-cpu]
+
+A step is one call of lynx_linear_sparse_lora (sparsify + 2:4 sparse-MFMA GEMM
+with the LoRA epilogue) on one batch of synthetic input already resident in
+HBM.  The default workload is the DiT MLP up-projection, X [4096 x 3072] ->
+Y [4096 x 12288], rank-64 LoRA.  Inputs rotate over three independent sets
+(X, W, LA, LB, Y, workspace) so the working set (> 600 MB) exceeds the 256 MB
+last-level cache.
+
+Also timed with the same protocol: the dense bf16 MFMA layer (lynx_linear_dense,
+the speedup baseline), the sparsifier alone and the GEMM alone (split of the
+sparse layer's time), and torch.matmul (hipBLASLt) as a sanity reference that
+the library never calls.  The CPU oracle is timed on a bounded sample on the
+host (cpu_baseline).  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_DENSE_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, AMD published
+PEAK_SPARSE_BF16_TFLOPS = 5033.2   # 2:4 structured-sparse bf16 (dense-equivalent), AMD published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="mlp_up", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--sets", type=int, default=3)
+    return p.parse_args()
+
+
+def time_region(fn, steps, warmup, stream):
+    """Average ms per call of fn(i) over `steps` calls, HIP events on `stream`."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(L, target_s=15.0):
+    """The fp64 oracle on a bounded sample of rows of the same workload."""
+    import numpy as np
+    from oracle import lynx_oracle as orc
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in info), default=os.cpu_count())
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    rows = 64
+    t0 = time.perf_counter()
+    orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
+    dt = time.perf_counter() - t0
+    # grow the sample to roughly target_s seconds of CPU work
+    rows = int(min(L.M, max(rows, rows * target_s / max(dt, 1e-3) * 0.8)))
+    t0 = time.perf_counter()
+    orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
+    dt = time.perf_counter() - t0
+    flops = 2 * rows * L.N * L.K + 2 * rows * L.R * (L.K + L.N)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": cores,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {rows} of {L.M} rows of the same {L.name} layer (full W, LA, LB), "
+                      f"fp64 NumPy oracle incl. selection, norms, and both contractions"}
+
+
+def traffic_for(kernel_src: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    with open(kernel_src, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()[:16]
+    return rec.get("bytes_per_launch") if rec.get("kernel_sha") == h else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the layer shards by rows with no communication; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import activation_sparse_gemm_amd as lynx
+    from workloads import make_config, make_layer
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    base = make_config(args.workload)[0]
+    M, K, N, R = base.M, base.K, base.N, base.R
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    sets = []
+    for s in range(args.sets):
+        L = base if s == 0 else make_layer(M, K, N, base.kind, seed=100 + s, R=R, name=base.name)
+        X, W, LA, LB = to_dev(L.X), to_dev(L.W), to_dev(L.LA), to_dev(L.LB)
+        ws = torch.empty(lynx.workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        packed = lynx.sparsify(X, LB)
+        sets.append(dict(X=X, W=W, LA=LA, LB=LB, ws=ws, Y=Y, Yd=Yd, packed=packed))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    S = len(sets)
+
+    def step(i):
+        d = sets[i % S]
+        lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"], Y=d["Y"], workspace=d["ws"])
+
+    def dense(i):
+        d = sets[i % S]
+        lynx.linear_dense(d["X"], d["W"], Y=d["Yd"])
+
+    def gemm_only(i):
+        d = sets[i % S]
+        v, m, sc, T = d["packed"]
+        lynx.linear_sparse_lora_packed(v, m, sc, T, d["W"], d["LA"], Y=d["Y"])
+
+    def sparsify_only(i):
+        d = sets[i % S]
+        v, m, sc, T = d["packed"]
+        lynx.sparsify(d["X"], d["LB"], out=dict(values=v, meta=m, scale=sc, T=T))
+
+    def torch_mm(i):
+        d = sets[i % S]
+        torch.matmul(d["X"], d["W"].t(), out=d["Yd"])
+
+    torch.cuda.synchronize()
+    ms = time_region(step, args.steps, args.warmup, stream)
+    ms_dense = time_region(dense, args.steps, args.warmup, stream)
+    ms_gemm = time_region(gemm_only, args.steps, args.warmup, stream)
+    ms_k1 = time_region(sparsify_only, args.steps, args.warmup, stream)
+    ms_torch = time_region(torch_mm, args.steps, args.warmup, stream)
+
+    flops = 2 * M * N * K + 2 * M * R * (K + N)           # dense-equivalent, whole layer
+    tflops = flops / (ms * 1e-3) / 1e12
+    # dominant kernel: the 2:4 GEMM; algorithmic flops = products on kept values
+    # (M N K/2 multiply-adds) + LoRA up-projection (M R N multiply-adds)
+    k2_alg_flops = M * N * K + 2 * M * R * N
+    k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
+    traffic = traffic_for(os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc", "k_gemm.hip"),
+                          args.workload)
+    cpu = None if args.no_cpu else cpu_baseline(base)
+
+    rec = {
+        "metric": "dense-equiv TFLOP/s of the sparse+LoRA linear (also % of bf16 sparse-MFMA "
+                  "peak and speedup vs the in-library dense bf16 GEMM), M4096 K3072",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{base.name}: X[{M}x{K}] bf16 -> Y[{M}x{N}], rank-{R} LoRA, "
+                               f"heavy-tailed activations, {S} rotating input sets",
+                   "M": M, "K": K, "N": N, "R": R},
+        "pct_sparse_peak": round(100 * tflops / PEAK_SPARSE_BF16_TFLOPS, 2),
+        "pct_dense_peak": round(100 * tflops / PEAK_DENSE_BF16_TFLOPS, 2),
+        "speedup_vs_dense": round(ms_dense / ms, 3),
+        "dense_tflops": round(2 * M * N * K / (ms_dense * 1e-3) / 1e12, 2),
+        "dense_ms": round(ms_dense, 5),
+        "split_ms": {"sparsify": round(ms_k1, 5), "sparse_gemm_lora": round(ms_gemm, 5)},
+        "torch_matmul_ms": round(ms_torch, 5),
+        "roofline": {"bound": "mfma", "kernel": "gemm_tiled<sparse> (2:4 SMFMAC + LoRA epilogue)",
+                     "achieved": round(k2_tflops, 2), "peak": PEAK_DENSE_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(k2_tflops / PEAK_DENSE_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,142 @@
+/*
+ * lynx.h - C ABI of the RT-Lynx sparse + LoRA linear layer for AMD MI355X (gfx950).
+ *
+ * The layer (RT-Lynx page, aitrends.kr, "RT-Lynx: Diffusion Transformers에서
+ * GEMM Sparsity를 Activation으로 옮겨 실현하는 방법"; section 방법론, item
+ * "핵심 메커니즘", and the two formulas of section 코드 예제):
+ *
+ *     X~   = X with, in every group of 4 consecutive input channels, only the
+ *            two entries of largest |x| kept (Top-K 2:4 activation selection)
+ *     s    = ||X||_2 / ||X~||_2 per token (row)      (Norm Compensation)
+ *     Y    = s * (X~ W^T) + (X LB^T) LA^T           (= S(X) W^T + X (LA LB)^T)
+ *
+ * Readings fixed by this library where the page is silent:
+ *   - groups are 4 consecutive channels of the reduction axis K, aligned at 0
+ *     mod 4; ties in |x| go to the lower channel index; -0 and +0 are equal;
+ *   - the page's eps is 0; a row whose X~ is zero (only an all-zero row) has s = 1;
+ *   - the LoRA branch takes the dense, unscaled X; no bias.
+ *
+ * Conventions common to every entry point
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are
+ *     contiguous and row-major; every pointer must be 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream).  The library never allocates device memory, never synchronizes
+ *     and keeps no per-call state, so calls are re-entrant; concurrent calls
+ *     that write the same buffers race, as with any kernel.
+ *   - All arguments are validated before anything is launched.  On an error
+ *     the status is returned and no output is written.
+ *   - Asynchronous device faults surface at the caller's next synchronization
+ *     with the stream, not as a status of the call that queued the work.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs.
+ *   - Shape limits: K is a positive multiple of 128; M >= 0 and N >= 0 (0 is a
+ *     no-op); R (LoRA rank) is one of 0, 16, 32, 48, 64 (0 = no LoRA branch);
+ *     M, N, K <= 2^24 and every tensor smaller than 2^31 elements.
+ *   - The current device must be gfx950 (MI350 series); otherwise
+ *     LYNX_ERR_UNSUPPORTED_DEVICE.
+ *
+ * Packed sparse operand (the 2:4 activation in the sparse matrix unit's
+ * format, which the page has the sparsifier emit directly):
+ *   values [M][K/2] bf16 : the two kept entries of every group, in ascending
+ *                          channel order, copied bit-exactly from X (unscaled);
+ *   meta   [M][K/8] uint8: a 4-bit code per group, (first kept position) |
+ *                          (second kept position) << 2, positions 0..3 inside
+ *                          the group, first < second; group 2j in the low
+ *                          nibble of byte j, group 2j+1 in the high nibble.
+ *                          Read as a little-endian 16-bit word per 16
+ *                          channels this is the sparse-index operand of
+ *                          v_smfmac_f32_16x16x64_bf16 for one lane;
+ *   scale  [M] fp32      : s per row;
+ *   T      [M][R] bf16   : X LB^T, the LoRA down-projection of the dense X.
+ */
+#ifndef LYNX_H
+#define LYNX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* lynx_stream_t; /* a hipStream_t */
+
+typedef enum lynx_status {
+    LYNX_OK = 0,
+    LYNX_ERR_NULL = 1,               /* a required pointer is NULL */
+    LYNX_ERR_SHAPE = 2,              /* a size is outside the limits above */
+    LYNX_ERR_ALIGN = 3,              /* a pointer is not 16-byte aligned */
+    LYNX_ERR_WORKSPACE = 4,          /* workspace is NULL or too small */
+    LYNX_ERR_DEVICE = 5,             /* a HIP call or a kernel launch failed */
+    LYNX_ERR_UNSUPPORTED_DEVICE = 6  /* the current device is not gfx950 */
+} lynx_status;
+
+/* Human-readable name of a status; never NULL. */
+const char* lynx_status_string(lynx_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int lynx_version(void);
+
+/*
+ * Bytes of device workspace lynx_linear_sparse_lora needs for an (M, K, R)
+ * problem: the packed operand (values, meta, scale) and T, each 256-byte
+ * aligned.  Returns 0 for invalid sizes.
+ */
+size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R);
+
+/*
+ * lynx_sparsify - online activation sparsification and LoRA down-projection.
+ * Page: 방법론 "핵심 메커니즘" (Top-K 2:4 selection, S(X) = s X~) and
+ * 핵심 기여 (pattern decision, Top-K and compression in one execution path,
+ * emitting the sparse-unit layout).  One read of X produces:
+ *   values [M][K/2], meta [M][K/8], scale [M]  - the packed operand above;
+ *   T [M][R] = X LB^T (fp32 accumulation, rounded to bf16), if R > 0.
+ * Inputs: X [M][K] bf16; LB [R][K] bf16 (NULL iff R == 0); T NULL iff R == 0.
+ */
+lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB,
+                          int64_t M, int64_t K, int64_t R,
+                          uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,
+                          lynx_stream_t stream);
+
+/*
+ * lynx_linear_sparse_lora - the whole layer Y = S(X) W^T + X (LA LB)^T.
+ * Page: 코드 예제, second formula; 방법론 "CUDA 커널 최적화" (the LoRA output
+ * is produced and accumulated on chip inside the sparse GEMM).
+ * Runs lynx_sparsify into `workspace`, then the 2:4 sparse-MFMA GEMM whose
+ * epilogue adds T LA^T and applies s, with fp32 accumulation and a bf16
+ * (round-to-nearest-even) store.
+ * Inputs: X [M][K], W [N][K], LA [N][R], LB [R][K] (LA, LB NULL iff R == 0).
+ * Output: Y [M][N] bf16.  workspace: >= lynx_workspace_bytes(M, K, R) bytes,
+ * 256-byte aligned, contents on entry irrelevant, clobbered.
+ */
+lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W,
+                                    const uint16_t* LA, const uint16_t* LB, uint16_t* Y,
+                                    int64_t M, int64_t N, int64_t K, int64_t R,
+                                    void* workspace, size_t workspace_bytes,
+                                    lynx_stream_t stream);
+
+/*
+ * lynx_linear_sparse_lora_packed - the GEMM half of the layer on an already
+ * packed operand: Y = scale * (X~ W^T) + T LA^T, X~ given by values + meta.
+ * Same page passages as lynx_linear_sparse_lora.  Used to time the sparse
+ * GEMM apart from the sparsifier.  T and LA NULL iff R == 0.
+ */
+lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t* meta,
+                                           const float* scale, const uint16_t* T,
+                                           const uint16_t* W, const uint16_t* LA, uint16_t* Y,
+                                           int64_t M, int64_t N, int64_t K, int64_t R,
+                                           lynx_stream_t stream);
+
+/*
+ * lynx_linear_dense - the dense layer Y = X W^T, bf16 MFMA, fp32 accumulate,
+ * bf16 store: the baseline the page's speedups are quoted against
+ * (주요 결과, speed/efficiency item).  No LoRA branch.
+ */
+lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y,
+                              int64_t M, int64_t N, int64_t K, lynx_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LYNX_H */

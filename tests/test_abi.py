@@ -1,0 +1,138 @@
+"""The C ABI: the library loads, exports every symbol the headers declare, and
+rejects bad arguments with the documented status before touching a device.
+
+No call here reaches a kernel launch: every argument set fails validation (or
+is a documented no-op) before the device is queried.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from activation_sparse_gemm_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE, UNSUPPORTED = range(7)
+
+A = 0x10000  # a fake, 16-byte-aligned address: validation fails before any use
+B = 0x20000
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(lynx_\w+)\s*\(", text))
+    return names
+
+
+def test_headers_declare_the_boundary():
+    names = declared_functions()
+    for required in ("lynx_sparsify", "lynx_linear_sparse_lora", "lynx_linear_sparse_lora_packed",
+                     "lynx_linear_dense", "lynx_workspace_bytes", "lynx_status_string"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = _abi.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert name in _abi.SIGNATURES, f"binding lacks {name}"
+
+
+def test_status_strings():
+    for s in range(7):
+        assert _abi.status_string(s).startswith(_abi.STATUS_NAMES[s])
+    assert "UNKNOWN" in _abi.status_string(99)
+
+
+def test_workspace_bytes():
+    ws = _abi.workspace_bytes(4096, 3072, 64)
+    # values M*K + meta M*K/8 + scale 4M + T 2MR, each 256-aligned
+    assert ws == 4096 * 3072 + 4096 * 3072 // 8 + 4096 * 4 + 4096 * 64 * 2
+    assert _abi.workspace_bytes(3, 128, 16) == 512 + 256 + 256 + 256  # 384 B of values rounds up
+    assert _abi.workspace_bytes(16, 100, 0) == 0      # K not a multiple of 128
+    assert _abi.workspace_bytes(16, 128, 8) == 0      # unsupported rank
+    assert _abi.workspace_bytes(-1, 128, 0) == 0
+
+
+def call_sparsify(X=A, LB=A, M=16, K=128, R=16, values=A, meta=A, scale=A, T=A):
+    return _abi.lib().lynx_sparsify(X, LB, M, K, R, values, meta, scale, T, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(K=64), SHAPE), (dict(M=-1), SHAPE),
+    (dict(R=8), SHAPE), (dict(R=80), SHAPE), (dict(M=1 << 25), SHAPE),
+    (dict(X=None), NULL), (dict(values=None), NULL), (dict(meta=None), NULL),
+    (dict(scale=None), NULL), (dict(LB=None), NULL), (dict(T=None), NULL),
+    (dict(X=A + 2), ALIGN), (dict(meta=A + 8), ALIGN), (dict(T=A + 4), ALIGN),
+    (dict(M=0), OK),
+])
+def test_sparsify_validation(kw, status):
+    assert call_sparsify(**kw) == status
+
+
+def call_linear(X=A, W=A, LA=A, LB=A, Y=A, M=16, N=16, K=128, R=16, ws=B, wsb=1 << 20):
+    return _abi.lib().lynx_linear_sparse_lora(X, W, LA, LB, Y, M, N, K, R, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=192), SHAPE), (dict(N=-3), SHAPE), (dict(R=17), SHAPE),
+    (dict(W=None), NULL), (dict(LA=None), NULL), (dict(Y=None), NULL),
+    (dict(Y=A + 2), ALIGN), (dict(ws=B + 16), ALIGN),
+    (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE),
+    (dict(N=0), OK), (dict(M=0), OK),
+])
+def test_linear_validation(kw, status):
+    assert call_linear(**kw) == status
+
+
+def test_linear_workspace_exact_boundary():
+    need = _abi.workspace_bytes(16, 128, 16)
+    assert call_linear(wsb=need - 1) == WORKSPACE
+
+
+def call_packed(v=A, m=A, s=A, T=A, W=A, LA=A, Y=A, M=16, N=16, K=128, R=16):
+    return _abi.lib().lynx_linear_sparse_lora_packed(v, m, s, T, W, LA, Y, M, N, K, R, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=1), SHAPE), (dict(R=100), SHAPE), (dict(v=None), NULL), (dict(T=None), NULL),
+    (dict(s=A + 4), ALIGN), (dict(LA=A + 2), ALIGN), (dict(M=0), OK),
+])
+def test_packed_validation(kw, status):
+    assert call_packed(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((A, A, A, 16, 16, 96), SHAPE), ((None, A, A, 16, 16, 128), NULL),
+    ((A, A, A + 6, 16, 16, 128), ALIGN), ((A, A, A, 0, 16, 128), OK),
+])
+def test_dense_validation(args, status):
+    assert _abi.lib().lynx_linear_dense(*args, None) == status
+
+
+def test_probe_validation():
+    L = _abi.lib()
+    assert L.lynx_probe_mfma(4, 0, A, A, A, A, None) == SHAPE
+    assert L.lynx_probe_mfma(0, 2, A, A, A, A, None) == SHAPE
+    assert L.lynx_probe_mfma(0, 0, A, A, None, A, None) == NULL
+    assert L.lynx_probe_mfma(1, 0, A + 1, A, A, A, None) == ALIGN
+
+
+def test_valid_arguments_without_gpu_report_unsupported_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
+    assert call_sparsify() == UNSUPPORTED
+    assert call_linear() == UNSUPPORTED
+
+
+def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        _abi.lib()

@@ -1,0 +1,117 @@
+"""lynx_sparsify (K1) against the CPU oracle.
+
+Bar: selected indices (through meta) and kept values bit-exact; scale within
+1e-5 relative; T within 5e-3 per-row relative error.  Shapes cover several
+row blocks with ragged tails, every supported rank, adversarial groups (ties,
+zeros, -0, +-1, denormals, extremes) and the full-size workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import activation_sparse_gemm_amd as lynx
+from oracle import lynx_oracle as orc
+from tests.gpu_util import (ROW_REL_TOL, SCALE_REL_TOL, dev, host_bits, host_f64, report,
+                            row_rel_err, say)
+from workloads import CONFIGS, make_activation, make_weights
+
+pytestmark = pytest.mark.gpu
+
+
+def check_sparsify(Xb, LBb, label, rows=None):
+    M, K = Xb.shape
+    say(f"sparsify {label} M={M} K={K} R={0 if LBb is None else LBb.shape[0]}")
+    values, meta, scale, T = lynx.sparsify(dev(Xb), None if LBb is None else dev(LBb))
+    torch.cuda.synchronize()
+    sel = slice(None) if rows is None else rows
+    ref = orc.sparsify(Xb[sel], LBb)
+    np.testing.assert_array_equal(meta.cpu().numpy()[sel], ref.meta, err_msg=f"{label}: meta")
+    np.testing.assert_array_equal(host_bits(values)[sel], ref.values, err_msg=f"{label}: values")
+    s = scale.cpu().numpy().astype(np.float64)[sel]
+    assert np.max(np.abs(s / ref.scale - 1)) <= SCALE_REL_TOL, f"{label}: scale"
+    if LBb is not None:
+        Tg = host_f64(T)[sel]
+        rep = report(f"{label} T", Tg, ref.T)
+        zero = np.linalg.norm(ref.T, axis=1) == 0
+        assert np.all(Tg[zero] == 0)
+        assert rep["max_row_rel"] <= ROW_REL_TOL and rep["nonfinite"] == 0
+
+
+@pytest.mark.parametrize("M,K,R", [
+    (256, 512, 64),    # the tiny workload
+    (1, 128, 16), (17, 256, 32), (100, 640, 48), (33, 1152, 64), (16, 128, 0), (255, 1024, 64),
+])
+def test_sparsify_shapes(M, K, R):
+    Xb = make_activation("heavy", M, K, seed=M + K)
+    LB = None if R == 0 else make_weights(8, K, R, seed=R)[2]
+    check_sparsify(Xb, LB, f"heavy {M}x{K}")
+
+
+def test_sparsify_gelu_input():
+    Xb = make_activation("gelu", 64, 3072, seed=3)
+    check_sparsify(Xb, make_weights(8, 3072, 64, seed=3)[2], "gelu 64x3072")
+
+
+def adversarial_rows(specials, M, K, seed):
+    rng = np.random.default_rng(seed)
+    Xb = specials[rng.integers(0, len(specials), size=(M, K))]
+    Xb[0] = 0                                   # zero row
+    Xb[1] = 0x8000                              # negative zeros
+    Xb[2] = np.where(rng.random(K) < 0.5, 0x3F80, 0xBF80)  # +-1: all ties, s = sqrt(2)
+    Xb[3, :] = 0x3F80                           # all equal
+    Xb[4] = 0                                   # one nonzero per group
+    Xb[4, ::4] = 0x4000
+    Xb[5] = rng.choice(np.array([0x0001, 0x8001, 0x0003, 0x007F], dtype=np.uint16), size=K)
+    return Xb
+
+
+def test_sparsify_extreme_magnitudes():
+    """Largest finite values and subnormals: selection, packing and s (fp64 path)."""
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x7F7F, 0xFF7F,
+                         0x3F80, 0xBF80, 0x4000, 0xC000], dtype=np.uint16)
+    Xb = adversarial_rows(specials, 48, 512, seed=0)
+    Xb[6] = 0x7F7F                              # every square overflows fp32
+    Xb[7, :256] = 0x0080                        # smallest normal next to subnormals
+    Xb[7, 256:] = 0x0001
+    check_sparsify(Xb, None, "extreme magnitudes")
+
+
+def test_sparsify_adversarial_groups_with_lora():
+    """Ties, zeros, -0, +-1 and subnormals with moderate magnitudes, T included."""
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x0080, 0x4780, 0xC780,
+                         0x3F80, 0xBF80, 0x4000, 0xC000], dtype=np.uint16)
+    Xb = adversarial_rows(specials, 48, 512, seed=1)
+    LB = make_weights(8, 512, 64, seed=0)[2]
+    check_sparsify(Xb, LB, "adversarial")
+
+
+def test_sparsify_is_deterministic():
+    Xb = make_activation("heavy", 300, 3072, seed=7)
+    LB = make_weights(8, 3072, 64, seed=7)[2]
+    X, L = dev(Xb), dev(LB)
+    a = [t.clone() for t in lynx.sparsify(X, L)]
+    b = lynx.sparsify(X, L)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y)
+
+
+@pytest.mark.parametrize("M,K,kind", sorted({(m, k, kind) for cfg in ("qkv", "mlp_down", "block")
+                                             for (m, k, n, kind) in CONFIGS[cfg]}))
+def test_sparsify_full_size(M, K, kind):
+    """Full-size activations: meta/values/scale on every row, T on sampled rows."""
+    Xb = make_activation(kind, M, K, seed=0)
+    LB = make_weights(8, K, 64, seed=0)[2]
+    say(f"sparsify full {M}x{K} {kind}")
+    values, meta, scale, T = lynx.sparsify(dev(Xb), dev(LB))
+    torch.cuda.synchronize()
+    idx = orc.select_top2_of_4(Xb)
+    np.testing.assert_array_equal(meta.cpu().numpy(), orc.pack_meta(idx))
+    np.testing.assert_array_equal(host_bits(values), orc.pack_values(Xb, idx))
+    s_ref = orc.norm_scale(orc.decode_bf16(Xb), orc.keep_mask(idx))
+    s = scale.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(s / s_ref - 1)) <= SCALE_REL_TOL
+    rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
+    T_ref = orc.decode_bf16(Xb[rows]) @ orc.decode_bf16(LB).T
+    assert row_rel_err(host_f64(T)[rows], T_ref).max() <= ROW_REL_TOL
