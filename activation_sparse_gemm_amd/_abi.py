@@ -97,12 +97,20 @@ def workspace_bytes(M: int, K: int, R: int) -> int:
     return lib().lynx_workspace_bytes(M, K, R)
 
 
+def padded_rows(M: int) -> int:
+    """Rows of the stored packed operand: whole 16-row tiles."""
+    return (M + 15) // 16 * 16
+
+
 def sparsify(X: torch.Tensor, LB: torch.Tensor | None = None, out: dict | None = None):
     """Packed 2:4 operand and LoRA down-projection of X (lynx_sparsify).
 
-    Returns (values [M, K/2] bf16, meta [M, K/8] uint8, scale [M] fp32, T [M, R] bf16 or None).
+    Returns (values, meta, scale, T): values (Mp*K/2,) bf16 and meta (Mp*K/8,)
+    uint8 in the 16-row x 64-channel tile order of lynx.h (Mp = M rounded up
+    to 16), scale [M] fp32, T [M, R] bf16 or None.
     """
     M, K = X.shape
+    Mp = padded_rows(M)
     R = 0 if LB is None else LB.shape[0]
     _need(X, torch.bfloat16, (M, K), "X")
     if LB is not None:
@@ -111,18 +119,18 @@ def sparsify(X: torch.Tensor, LB: torch.Tensor | None = None, out: dict | None =
     out = out or {}
     values = out.get("values")
     if values is None:
-        values = torch.empty((M, K // 2), dtype=torch.bfloat16, device=dev)
+        values = torch.empty((Mp * K // 2,), dtype=torch.bfloat16, device=dev)
     meta = out.get("meta")
     if meta is None:
-        meta = torch.empty((M, K // 8), dtype=torch.uint8, device=dev)
+        meta = torch.empty((Mp * K // 8,), dtype=torch.uint8, device=dev)
     scale = out.get("scale")
     if scale is None:
         scale = torch.empty((M,), dtype=torch.float32, device=dev)
     T = out.get("T")
     if T is None and R > 0:
         T = torch.empty((M, R), dtype=torch.bfloat16, device=dev)
-    _need(values, torch.bfloat16, (M, K // 2), "values")
-    _need(meta, torch.uint8, (M, K // 8), "meta")
+    _need(values, torch.bfloat16, (Mp * K // 2,), "values")
+    _need(meta, torch.uint8, (Mp * K // 8,), "meta")
     _need(scale, torch.float32, (M,), "scale")
     if R > 0:
         _need(T, torch.bfloat16, (M, R), "T")
@@ -157,12 +165,12 @@ def linear_sparse_lora(X, W, LA=None, LB=None, Y=None, workspace=None):
 
 def linear_sparse_lora_packed(values, meta, scale, T, W, LA=None, Y=None):
     """Y = scale * (X~ W^T) + T LA^T from a packed operand (lynx_linear_sparse_lora_packed)."""
-    M = values.shape[0]
-    K = values.shape[1] * 2
-    N = W.shape[0]
+    M = scale.shape[0]
+    N, K = W.shape
+    Mp = padded_rows(M)
     R = 0 if LA is None else LA.shape[1]
-    _need(values, torch.bfloat16, (M, K // 2), "values")
-    _need(meta, torch.uint8, (M, K // 8), "meta")
+    _need(values, torch.bfloat16, (Mp * K // 2,), "values")
+    _need(meta, torch.uint8, (Mp * K // 8,), "meta")
     _need(scale, torch.float32, (M,), "scale")
     _need(W, torch.bfloat16, (N, K), "W")
     if R > 0:

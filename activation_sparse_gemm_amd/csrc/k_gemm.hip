@@ -11,14 +11,24 @@
 // per mille, so that rounding is far below the output's own bf16 rounding).
 //
 // Tiling: one 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave
-// 128 x 128 = 8 x 8 accumulator tiles of 16 x 16 (256 fp32 per lane).  The K
-// loop moves 64 dense channels per stage through LDS, double-buffered; global
-// loads for stage t+1 are in flight while stage t is multiplied.
-//   sparse stage: A = packed values 256 rows x 64 B, meta 256 rows x 8 B,
-//                 B = W 256 rows x 128 B               (50 KB)
-//   dense stage:  A = X 256 rows x 128 B, B = W 256 rows x 128 B   (64 KB)
-// LDS rows are stored with their 16-byte chunks XOR-swizzled by row so that
-// the 16-byte fragment reads of 8 (or 16) consecutive lanes hit distinct banks.
+// 128 x 128 = 8 x 8 accumulator tiles of 16 x 16 (256 fp32 per lane, in AGPRs).
+// Operands move global -> LDS by buffer_load ... lds (no VGPR staging) into a
+// ring of LDS stages of 64 dense channels:
+//   sparse: A = packed values 256 x 64 B, meta 256 x 8 B, B = W 256 x 128 B
+//           (50 KB, 1024 matrix-core cycles per wave); ring of 3 (150 KB),
+//           loads issued 2 stages ahead.  The packed operand is stored in
+//           16-row x 64-channel tiles, so a stage's A side is 16 contiguous
+//           1 KB value tiles and 16 contiguous 128 B meta tiles;
+//   dense:  32 channels per stage: A = X 256 x 64 B, B = W 256 x 64 B
+//           (32 KB, 1024 cycles); ring of 4 (128 KB), loads issued 3 ahead.
+// The sparse A side is read as whole 128-byte lines, which keeps the L1 -> L2
+// request rate (about one line per clock per CU) below the matrix-core rate.
+// The loads of a stage are waited for with an explicit vmcnt that leaves the
+// later stages' loads in flight, then one s_barrier per stage.  Rows past M or
+// N lie past the end of their buffer resource and are never read (their LDS
+// slots keep stale values, which only reach outputs that are not stored).
+// LDS rows keep their 16-byte chunks XOR-swizzled by row so the fragment reads
+// of 8 (and 16) consecutive lanes hit distinct banks.
 //
 // Register layouts (pinned by the probe tests), lane l, r = l % 16, q = l / 16:
 //   v_smfmac_f32_16x16x64_bf16: A = row r, dense channels [16q, 16q+16) as 8
@@ -36,24 +46,38 @@
 namespace lynx {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256, GROUP_M = 8;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256, BN = 256, NT = 256, GROUP_M = 8;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit format
 
 template <bool SPARSE>
 struct Cfg {
-    static constexpr int A_ROW = SPARSE ? 64 : 128;  // bytes per A row per stage
+    static constexpr int BK = SPARSE ? 64 : 32;          // dense channels per stage
+    static constexpr int A_ROW = 64;                     // LDS bytes per A row per stage
+    static constexpr int B_ROW = SPARSE ? 128 : 64;      // LDS bytes per B row per stage
     static constexpr int A_BYTES = BM * A_ROW;
     static constexpr int META_BYTES = SPARSE ? BM * 8 : 0;
-    static constexpr int B_BYTES = BN * 128;
+    static constexpr int B_BYTES = BN * B_ROW;
     static constexpr int STAGE = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int A_LOADS = A_BYTES / 16 / NT;  // 16-byte chunks per thread
-    static constexpr int B_LOADS = B_BYTES / 16 / NT;
-    static constexpr int EPI_OFF = 64 * 1024;             // epilogue scratch, 4 KB per wave
-    static constexpr int LDS = (2 * STAGE > EPI_OFF + 4 * 4096) ? 2 * STAGE : EPI_OFF + 4 * 4096;
+    static constexpr int NSTAGE = SPARSE ? 3 : 4;
+    static constexpr int A_DMA = A_BYTES / 1024 / 4;     // 1 KB DMA instructions per wave
+    static constexpr int B_DMA = B_BYTES / 1024 / 4;
+    static constexpr int M_DMA = META_BYTES / 256 / 4;   // 256 B (dword) DMA instructions
+    static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + M_DMA;
+    static constexpr int EPI_OFF = 64 * 1024;            // epilogue scratch, 4 KB per wave
+    static constexpr int SCALE_OFF = NSTAGE * STAGE;     // s of the tile's 256 rows (sparse)
+    static constexpr int LDS = NSTAGE * STAGE + (SPARSE ? BM * 4 : 0);
+    static_assert(LDS >= EPI_OFF + 4 * 4096, "epilogue scratch must fit");
+    static_assert(LDS <= 160 * 1024, "LDS budget");
+    static_assert(NSTAGE >= 3 && NSTAGE <= 4, "ring depth handled by the waits below");
+    static_assert(NSTAGE * STAGE >= 64 * 1024 + 4 * 4096, "LoRA tiles and epilogue scratch");
+    static_assert((NSTAGE - 1) * DMA_PER_STAGE < 64, "vmcnt range");
 };
 
-// chunk swizzles (16-byte chunk index within a row)
-__device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// 16-byte chunk swizzles within 64-byte and 128-byte rows
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
@@ -69,6 +93,47 @@ __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& 
     tn = in / gm;
 }
 
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4{int(uint32_t(p)), int(uint32_t(p >> 32) & 0xFFFFu), int(bytes), kRsrcWord3};
+}
+
+// One wave-wide global -> LDS copy: lane l's 16 (or 4) bytes at
+// rsrc + voff + soff land at LDS byte lds + 16 l (or 4 l).  The buffer range
+// check covers voff only, so voff carries the row and soff the k offset.
+__device__ __forceinline__ void dma16(uint32_t lds, int voff, i32x4 rsrc, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, int voff, i32x4 rsrc, int soff) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) (n < 64), leaving lgkmcnt / expcnt alone
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0): own LDS reads done, vector loads down to n
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+__device__ __forceinline__ void block_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read(const char* smem, int off) {
     return *reinterpret_cast<const T*>(smem + off);
@@ -78,7 +143,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
            (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
 }
-
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
@@ -92,10 +156,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
     const uint16_t* __restrict__ LA,     // SPARSE only: [N][R] or null
     uint16_t* __restrict__ Y, int M, int N, int K, int R) {
     using C = Cfg<SPARSE>;
-    __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, q = lane >> 4;
     const int wm = wave & 1, wn = wave >> 1;
 
@@ -104,64 +169,74 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // ---- staging: buffer loads (rows past M or N read as zero) -------------
-    // Thread tid moves chunk c = tid + 256 j (j = 0..) of each operand per stage.
-    // Consecutive j are a fixed number of rows apart, so one per-thread byte
-    // offset plus a uniform per-j offset addresses every chunk, and the LDS
-    // swizzle (a function of row % 16) is the same for every j.
-    const int rowbytesA = SPARSE ? K : 2 * K;  // packed values: K/2 bf16 per row
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(Aptr), (short)0, M * rowbytesA, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(W), (short)0, N * 2 * K, 0x00020000);
-    constexpr int A_ROWS_PER_J = SPARSE ? 64 : 32;  // NT chunks cover this many rows
-    int voffA, dstA0;
-    if constexpr (SPARSE) {
-        const int row = tid >> 2, ch = tid & 3;
-        voffA = (m0 + row) * rowbytesA + ch * 16;
-        dstA0 = row * 64 + 16 * (ch ^ swz64(row));
-    } else {
-        const int row = tid >> 3, ch = tid & 7;
-        voffA = (m0 + row) * rowbytesA + ch * 16;
-        dstA0 = row * 128 + 16 * (ch ^ swz128(row));
+    // ---- DMA addressing --------------------------------------------------
+    // sparse A: instruction j of wave w moves the 1 KB value tile of row block
+    //   (m0/16 + w + 4j) into LDS rows 16 (w + 4j) .. +16 (64 B each);
+    // sparse meta (dword DMA, 256 B): the two 128 B tiles of row blocks
+    //   2 (w + 4j), 2 (w + 4j) + 1 into LDS rows 32 (w + 4j) .. +32 (8 B each);
+    // sparse W (128-byte LDS rows): instruction j moves rows 8 (w + 4j) + l/8;
+    // dense X and W (64-byte LDS rows): instruction j moves rows 16 (w + 4j) + l/4.
+    // Lane l lands at LDS byte 16 l (4 l) of the instruction's 1 KB (256 B);
+    // its source is the chunk the row's swizzle puts there.
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+    const int steps = K / 64;
+    const int Mp = (M + 15) & ~15;
+    const i32x4 rsA = SPARSE ? make_rsrc(Aptr, uint32_t(Mp) * uint32_t(K))
+                             : make_rsrc(Aptr, uint32_t(M) * uint32_t(2 * K));
+    const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
+    i32x4 rsM = {0, 0, 0, 0};
+    if constexpr (SPARSE) rsM = make_rsrc(meta, uint32_t(Mp) * uint32_t(K / 8));
+
+    int voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA > 0 ? C::M_DMA : 1];
+#pragma unroll
+    for (int j = 0; j < C::A_DMA; ++j) {
+        if constexpr (SPARSE) {
+            const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
+            voffA[j] = (m0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
+        } else {
+            const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
+            voffA[j] = (m0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+        }
     }
-    const int voffB = (n0 + (tid >> 3)) * 2 * K + (tid & 7) * 16;
-    const int dstB0 = C::A_BYTES + C::META_BYTES + (tid >> 3) * 128 +
-                      16 * ((tid & 7) ^ swz128(tid >> 3));
-    __amdgpu_buffer_rsrc_t rsM;
-    int voffM = 0;
+#pragma unroll
+    for (int j = 0; j < C::B_DMA; ++j) {
+        if constexpr (SPARSE) {
+            const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
+            voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz128(row));
+        } else {
+            const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
+            voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+        }
+    }
     if constexpr (SPARSE) {
-        rsM = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(meta), (short)0, M * (K / 8),
-                                                0x00020000);
-        voffM = (m0 + tid) * (K / 8);
+#pragma unroll
+        for (int j = 0; j < C::M_DMA; ++j) {
+            const int blk = 2 * (wave + 4 * j) + (lane >> 5);
+            voffM[j] = (m0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
+        }
     }
 
-    u32x4 stA[C::A_LOADS], stB[C::B_LOADS];
-    u32x2 stM = {0u, 0u};
-
-    auto load_global = [&](int kk) {
-        const int kbA = SPARSE ? kk : 2 * kk;  // byte offset of this stage in an A row
+    // loads of k-stage t into ring slot t % NSTAGE (k offsets in bytes)
+    auto issue_stage = [&](int t) {
+        const uint32_t base = lds0 + uint32_t((t % C::NSTAGE) * C::STAGE);
+        const int kA = SPARSE ? t * 1024 : t * 64;
 #pragma unroll
-        for (int j = 0; j < C::A_LOADS; ++j)
-            stA[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsA, voffA, j * A_ROWS_PER_J * rowbytesA + kbA, 0));
+        for (int j = 0; j < C::A_DMA; ++j) dma16(base + 1024 * (wave + 4 * j), voffA[j], rsA, kA);
+        if constexpr (SPARSE) {
 #pragma unroll
-        for (int j = 0; j < C::B_LOADS; ++j)
-            stB[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rsB, voffB, j * 32 * 2 * K + 2 * kk, 0));
-        if constexpr (SPARSE)
-            stM = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsM, voffM, kk / 8, 0));
-    };
-    auto store_lds = [&](char* buf) {
+            for (int j = 0; j < C::M_DMA; ++j)
+                dma4(base + C::A_BYTES + 256 * (wave + 4 * j), voffM[j], rsM, t * 128);
+        }
 #pragma unroll
-        for (int j = 0; j < C::A_LOADS; ++j) *reinterpret_cast<u32x4*>(buf + dstA0 + 4096 * j) = stA[j];
-#pragma unroll
-        for (int j = 0; j < C::B_LOADS; ++j) *reinterpret_cast<u32x4*>(buf + dstB0 + 4096 * j) = stB[j];
-        if constexpr (SPARSE) *reinterpret_cast<u32x2*>(buf + C::A_BYTES + tid * 8) = stM;
+        for (int j = 0; j < C::B_DMA; ++j)
+            dma16(base + C::A_BYTES + C::META_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB,
+                  t * C::B_ROW);
     };
 
     // ---- per-lane fragment offsets (swizzle depends on row % 16 = r only) --
-    const int sw128 = swz128(r), sw64 = swz64(r);
+    const int s64 = swz64(r), s128 = swz128(r);
+    (void)s64;
     const int rowA = wm * 128 + r, rowB = wn * 128 + r;
 
     f32x4 acc[8][8];
@@ -170,16 +245,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
-    load_global(0);
-    store_lds(smem);
-    __syncthreads();
+    const int nk = K / C::BK;
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (SPARSE) {
+        // s of the tile's 256 rows into LDS (rows past M repeat the last row)
+        reinterpret_cast<float*>(smem + C::SCALE_OFF)[tid] = scale[min(m0 + tid, M - 1)];
+    }
+
+    // prologue: NSTAGE - 1 stages in flight
+#pragma unroll
+    for (int t = 0; t < C::NSTAGE - 1; ++t)
+        if (t < nk) issue_stage(t);
+    if (nk >= C::NSTAGE - 1) {
+        wait_vmcnt<(C::NSTAGE - 2) * C::DMA_PER_STAGE>();
+    } else {
+        __builtin_amdgcn_s_waitcnt(0);
+    }
+    block_barrier();
 
     for (int t = 0; t < nk; ++t) {
-        char* cur = smem + (t & 1) * C::STAGE;
-        char* nxt = smem + ((t + 1) & 1) * C::STAGE;
-        if (t + 1 < nk) load_global((t + 1) * BK);
-
+        if (t + C::NSTAGE - 1 < nk) issue_stage(t + C::NSTAGE - 1);
+        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
         if constexpr (SPARSE) {
             const char* As = cur;
             const char* Ms = cur + C::A_BYTES;
@@ -188,15 +274,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 const int base = (rowB + 16 * b) * 128;
-                const bf16x8 lo = lds_read<bf16x8>(Bs, base + 16 * (q ^ sw128));
-                const bf16x8 hi = lds_read<bf16x8>(Bs, base + 16 * ((4 + q) ^ sw128));
+                const bf16x8 lo = lds_read<bf16x8>(Bs, base + 16 * (q ^ s128));
+                const bf16x8 hi = lds_read<bf16x8>(Bs, base + 16 * ((4 + q) ^ s128));
                 bfr[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
                                                  12, 13, 14, 15);
             }
 #pragma unroll
             for (int a = 0; a < 8; ++a) {
                 const int row = rowA + 16 * a;
-                const bf16x8 afr = lds_read<bf16x8>(As, row * 64 + 16 * (q ^ sw64));
+                const bf16x8 afr = lds_read<bf16x8>(As, row * 64 + 16 * (q ^ s64));
                 const int idx = lds_read<uint16_t>(Ms, row * 8 + 2 * q);
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
@@ -206,65 +292,79 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
         } else {
             const char* As = cur;
             const char* Bs = cur + C::A_BYTES;
+            bf16x8 bfr[8];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                bf16x8 bfr[8];
+            for (int b = 0; b < 8; ++b)
+                bfr[b] = lds_read<bf16x8>(Bs, (rowB + 16 * b) * 64 + 16 * (q ^ s64));
+#pragma unroll
+            for (int a = 0; a < 8; ++a) {
+                const bf16x8 afr = lds_read<bf16x8>(As, (rowA + 16 * a) * 64 + 16 * (q ^ s64));
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
-                    bfr[b] = lds_read<bf16x8>(Bs, (rowB + 16 * b) * 128 + 16 * ((4 * ks + q) ^ sw128));
-#pragma unroll
-                for (int a = 0; a < 8; ++a) {
-                    const bf16x8 afr =
-                        lds_read<bf16x8>(As, (rowA + 16 * a) * 128 + 16 * ((4 * ks + q) ^ sw128));
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b],
-                                                                            0, 0, 0);
-                }
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b], 0,
+                                                                        0, 0);
             }
         }
-
-        if (t + 1 < nk) store_lds(nxt);
-        __syncthreads();
+        if (t + 1 < nk) {
+            // wait for stage t+1; the stages issued after it may stay in flight
+            const int later = min(nk - 2 - t, C::NSTAGE - 2);
+            if (later == C::NSTAGE - 2) {
+                wait_vmcnt<(C::NSTAGE - 2) * C::DMA_PER_STAGE>();
+            } else if (C::NSTAGE == 4 && later == 1) {
+                wait_vmcnt<C::DMA_PER_STAGE>();
+            } else {
+                __builtin_amdgcn_s_waitcnt(0);
+            }
+            block_barrier();
+        }
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // all waves done with the ring before LDS is reused
 
     // ---- LoRA up-projection: acc += (T / s) LA^T  ----------------------------
     if constexpr (SPARSE) {
         if (R > 0) {
-            // stage T / s (rows m0..) and LA (rows n0..), 256 x 64 bf16 each,
-            // zero beyond R, same swizzled 128-byte rows as the dense tiles
+            // T / s (rows m0..) and LA (rows n0..), 256 x 64 bf16 each, zero past
+            // R, in swizzled 128-byte rows.  All loads are issued before any is
+            // used (clamped in-bounds addresses; out-of-range chunks are zeroed).
             char* Ts = smem;
             char* Ls = smem + 32 * 1024;
+            const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
+            u32x4 traw[8], lraw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = tid + NT * j;
+                const int row = c >> 3, kc = min(8 * (c & 7), R - 8);
+                traw[j] = *reinterpret_cast<const u32x4*>(T + size_t(min(m0 + row, M - 1)) * R + kc);
+                lraw[j] = *reinterpret_cast<const u32x4*>(LA + size_t(min(n0 + row, N - 1)) * R + kc);
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int c = tid + NT * j;
                 const int row = c >> 3, ch = c & 7;
                 const int off = row * 128 + 16 * (ch ^ swz128(row));
-                u32x4 tv = {0u, 0u, 0u, 0u}, lv = {0u, 0u, 0u, 0u};
-                if (ch * 8 < R) {
-                    const int gm = min(m0 + row, M - 1);
-                    const u32x4 raw = *reinterpret_cast<const u32x4*>(T + size_t(gm) * R + ch * 8);
-                    const float inv = 1.0f / scale[gm];
-                    tv.x = pack_bf16x2(bf16_lo(raw.x) * inv, bf16_hi(raw.x) * inv);
-                    tv.y = pack_bf16x2(bf16_lo(raw.y) * inv, bf16_hi(raw.y) * inv);
-                    tv.z = pack_bf16x2(bf16_lo(raw.z) * inv, bf16_hi(raw.z) * inv);
-                    tv.w = pack_bf16x2(bf16_lo(raw.w) * inv, bf16_hi(raw.w) * inv);
-                    lv = *reinterpret_cast<const u32x4*>(LA + size_t(min(n0 + row, N - 1)) * R +
-                                                          ch * 8);
-                }
-                *reinterpret_cast<u32x4*>(Ts + off) = tv;
-                *reinterpret_cast<u32x4*>(Ls + off) = lv;
+                const bool live = 8 * ch < R;
+                const float inv = 1.0f / s_lds[row];
+                const u32x4 raw = traw[j];
+                u32x4 tv;
+                tv.x = pack_bf16x2(bf16_lo(raw.x) * inv, bf16_hi(raw.x) * inv);
+                tv.y = pack_bf16x2(bf16_lo(raw.y) * inv, bf16_hi(raw.y) * inv);
+                tv.z = pack_bf16x2(bf16_lo(raw.z) * inv, bf16_hi(raw.z) * inv);
+                tv.w = pack_bf16x2(bf16_lo(raw.w) * inv, bf16_hi(raw.w) * inv);
+                const u32x4 zero = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(Ts + off) = live ? tv : zero;
+                *reinterpret_cast<u32x4*>(Ls + off) = live ? lraw[j] : zero;
             }
             __syncthreads();
             for (int ks = 0; ks < (R + 31) / 32; ++ks) {
                 bf16x8 bfr[8];
 #pragma unroll
                 for (int b = 0; b < 8; ++b)
-                    bfr[b] = lds_read<bf16x8>(Ls, (rowB + 16 * b) * 128 + 16 * ((4 * ks + q) ^ sw128));
+                    bfr[b] = lds_read<bf16x8>(Ls, (rowB + 16 * b) * 128 + 16 * ((4 * ks + q) ^ s128));
 #pragma unroll
                 for (int a = 0; a < 8; ++a) {
                     const bf16x8 afr =
-                        lds_read<bf16x8>(Ts, (rowA + 16 * a) * 128 + 16 * ((4 * ks + q) ^ sw128));
+                        lds_read<bf16x8>(Ts, (rowA + 16 * a) * 128 + 16 * ((4 * ks + q) ^ s128));
 #pragma unroll
                     for (int b = 0; b < 8; ++b)
                         acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b],
@@ -280,11 +380,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
         const int row_l = 16 * a + 4 * q;  // row within the wave tile of element e = 0
-        float s4[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (SPARSE) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) s4[e] = scale[min(m0 + wm * 128 + row_l + e, M - 1)];
-        }
+        f32x4 s4 = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (SPARSE)
+            s4 = *reinterpret_cast<const f32x4*>(smem + C::SCALE_OFF + 4 * (wm * 128 + row_l));
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll

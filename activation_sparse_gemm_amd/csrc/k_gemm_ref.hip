@@ -79,8 +79,11 @@ __global__ __launch_bounds__(256) void gemm_sparse_ref(
         bf16x16 B[2];
 #pragma unroll
         for (int a = 0; a < 2; ++a) {
-            A[a] = *reinterpret_cast<const bf16x8*>(values + size_t(am[a]) * (K / 2) + kk / 2 + 8 * q);
-            I[a] = *reinterpret_cast<const uint16_t*>(meta + size_t(am[a]) * (K / 8) + kk / 8 + 2 * q);
+            // packed operand in 16-row x 64-channel tiles (512 values, 128 meta bytes)
+            const size_t tile = size_t(am[a] >> 4) * size_t(K / 64) + size_t(kk / 64);
+            const int rr = am[a] & 15;
+            A[a] = *reinterpret_cast<const bf16x8*>(values + tile * 512 + rr * 32 + 8 * q);
+            I[a] = *reinterpret_cast<const uint16_t*>(meta + tile * 128 + rr * 8 + 2 * q);
         }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {

@@ -12,7 +12,9 @@
 //   lane l: row r = l % 16, quarter q = l / 16; in chunk c it owns channels
 //   [128c + 32q, 128c + 32q + 32): 8 groups of 4, loaded as 4 x 16 bytes.
 //   - selection + packing in registers: 16 kept values (32 B) and 8 codes (4 B)
-//     per lane and chunk, stored contiguously;
+//     per lane and chunk, stored in the 16-row x 64-channel tile order of the
+//     packed operand (a workgroup's 16 rows are exactly one tile row-block;
+//     rows past M are written as zero values and codes (0,1));
 //   - row norms ||x||^2 and ||x~||^2 with v_dot2_f32_bf16 (products of bf16 are
 //     exact in fp32), summed per chunk in fp32 then in fp64;
 //   - T: the lane's 32 channels are the A operand of 4 v_mfma_f32_16x16x32_bf16
@@ -107,8 +109,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     const int nchunks = K / kChunk;
 
     const uint16_t* xrow = X + size_t(row_ok ? row : M - 1) * size_t(K);
-    uint16_t* vrow = values + size_t(row) * size_t(K / 2);
-    uint8_t* mrow = meta + size_t(row) * size_t(K / 8);
+    // packed operand, tile order: tile (block b, 64-channel step s) holds 16 rows
+    // x 32 values (1 KB) and 16 rows x 8 meta bytes (128 B)
+    const int steps = K / 64;
+    uint16_t* vtile = values + size_t(blockIdx.x) * size_t(steps) * 512 + r * 32;
+    uint8_t* mtile = meta + size_t(blockIdx.x) * size_t(steps) * 128 + r * 8;
 
     f32x4 acc[RT > 0 ? RT : 1];
 #pragma unroll
@@ -153,11 +158,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         n2 += double(pn);
         nt2 += double(pt);
 
-        if (row_ok) {
-            u32x4* vdst = reinterpret_cast<u32x4*>(vrow + k / 2);
-            vdst[0] = u32x4{kept[0], kept[1], kept[2], kept[3]};
-            vdst[1] = u32x4{kept[4], kept[5], kept[6], kept[7]};
-            *reinterpret_cast<uint32_t*>(mrow + k / 8) = code;
+        {
+            // channels k .. k+31 = half (q & 1) of step k / 64
+            const int step = k >> 6, half = q & 1;
+            u32x4* vdst = reinterpret_cast<u32x4*>(vtile + step * 512 + half * 16);
+            uint32_t* mdst = reinterpret_cast<uint32_t*>(mtile + step * 128 + half * 4);
+            if (row_ok) {
+                vdst[0] = u32x4{kept[0], kept[1], kept[2], kept[3]};
+                vdst[1] = u32x4{kept[4], kept[5], kept[6], kept[7]};
+                *mdst = code;
+            } else {
+                vdst[0] = u32x4{0u, 0u, 0u, 0u};
+                vdst[1] = u32x4{0u, 0u, 0u, 0u};
+                *mdst = 0x44444444u;
+            }
         }
 
         // T += X LB^T over these channels

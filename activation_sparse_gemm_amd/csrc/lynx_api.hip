@@ -32,10 +32,11 @@ struct WorkspaceLayout {
 };
 
 WorkspaceLayout layout_for(int64_t M, int64_t K, int64_t R) {
+    const size_t Mp = size_t((M + 15) / 16) * 16;  // packed operand rows, whole 16-row tiles
     WorkspaceLayout L;
     L.values = 0;
-    L.meta = L.values + round_up256(size_t(M) * size_t(K / 2) * 2);
-    L.scale = L.meta + round_up256(size_t(M) * size_t(K / 8));
+    L.meta = L.values + round_up256(Mp * size_t(K / 2) * 2);
+    L.scale = L.meta + round_up256(Mp * size_t(K / 8));
     L.T = L.scale + round_up256(size_t(M) * 4);
     L.total = L.T + round_up256(size_t(M) * size_t(R) * 2);
     return L;

@@ -19,7 +19,8 @@
  * Conventions common to every entry point
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Every tensor pointer is a DEVICE pointer owned by the caller; tensors are
- *     contiguous and row-major; every pointer must be 16-byte aligned.
+ *     contiguous; X, W, LA, LB, T and Y are row-major, the packed operand is
+ *     stored as described below; every pointer must be 16-byte aligned.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
  *     stream).  The library never allocates device memory, never synchronizes
  *     and keeps no per-call state, so calls are re-entrant; concurrent calls
@@ -36,18 +37,25 @@
  *     LYNX_ERR_UNSUPPORTED_DEVICE.
  *
  * Packed sparse operand (the 2:4 activation in the sparse matrix unit's
- * format, which the page has the sparsifier emit directly):
- *   values [M][K/2] bf16 : the two kept entries of every group, in ascending
- *                          channel order, copied bit-exactly from X (unscaled);
- *   meta   [M][K/8] uint8: a 4-bit code per group, (first kept position) |
- *                          (second kept position) << 2, positions 0..3 inside
- *                          the group, first < second; group 2j in the low
- *                          nibble of byte j, group 2j+1 in the high nibble.
- *                          Read as a little-endian 16-bit word per 16
- *                          channels this is the sparse-index operand of
- *                          v_smfmac_f32_16x16x64_bf16 for one lane;
- *   scale  [M] fp32      : s per row;
- *   T      [M][R] bf16   : X LB^T, the LoRA down-projection of the dense X.
+ * format, which the page has the sparsifier emit directly).  Per row:
+ *   values row, K/2 bf16: the two kept entries of every group, in ascending
+ *                channel order, copied bit-exactly from X (unscaled);
+ *   meta row, K/8 bytes: a 4-bit code per group, (first kept position) |
+ *                (second kept position) << 2, positions 0..3 inside the group,
+ *                first < second; group 2j in the low nibble of byte j,
+ *                group 2j+1 in the high nibble.
+ * Storage order: tiles of 16 rows x 64 channels, the A operand of one
+ * v_smfmac_f32_16x16x64_bf16 step, each tile contiguous.  With
+ * Mp = M rounded up to a multiple of 16:
+ *   values [Mp/16][K/64][16][32] bf16  (Mp * K/2 elements): kept value j of
+ *          row m at ((m/16)*(K/64) + j/32)*512 + (m%16)*32 + j%32;
+ *   meta   [Mp/16][K/64][16][8] uint8  (Mp * K/8 bytes): meta byte j of row m
+ *          at ((m/16)*(K/64) + j/8)*128 + (m%16)*8 + j%8.
+ * Rows M..Mp-1 are written as zero values and meta 0x44 (positions 0 and 1).
+ * The 8 meta bytes of a row and step, read as four little-endian 16-bit
+ * words, are the sparse-index operands of the row's four lane groups.
+ *   scale  [M] fp32  : s per row;
+ *   T      [M][R] bf16 (row-major): X LB^T, the LoRA down-projection of X.
  */
 #ifndef LYNX_H
 #define LYNX_H
@@ -79,8 +87,8 @@ int lynx_version(void);
 
 /*
  * Bytes of device workspace lynx_linear_sparse_lora needs for an (M, K, R)
- * problem: the packed operand (values, meta, scale) and T, each 256-byte
- * aligned.  Returns 0 for invalid sizes.
+ * problem: the packed operand (values Mp*K bytes, meta Mp*K/8, scale 4M) and
+ * T (2MR), each 256-byte aligned.  Returns 0 for invalid sizes.
  */
 size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R);
 
@@ -89,7 +97,7 @@ size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R);
  * Page: 방법론 "핵심 메커니즘" (Top-K 2:4 selection, S(X) = s X~) and
  * 핵심 기여 (pattern decision, Top-K and compression in one execution path,
  * emitting the sparse-unit layout).  One read of X produces:
- *   values [M][K/2], meta [M][K/8], scale [M]  - the packed operand above;
+ *   values (Mp*K/2 bf16), meta (Mp*K/8 bytes), scale [M] - the packed operand;
  *   T [M][R] = X LB^T (fp32 accumulation, rounded to bf16), if R > 0.
  * Inputs: X [M][K] bf16; LB [R][K] bf16 (NULL iff R == 0); T NULL iff R == 0.
  */

@@ -33,7 +33,9 @@ notes of the repository):
   6. The packed format is the one the gfx950 sparse MFMA reads for its A
      operand (see pack_meta): kept values in ascending channel order, and a
      4-bit code per group, first kept position in bits 0-1, second in bits
-     2-3, two groups per byte with the even group in the low nibble.
+     2-3, two groups per byte with the even group in the low nibble.  In
+     memory both are stored in tiles of 16 rows x 64 channels (the operand
+     tile of one v_smfmac_f32_16x16x64_bf16 step): see tile_rows.
 
 Everything is computed in fp64 from exactly decoded bf16 inputs.
 """
@@ -161,15 +163,59 @@ def unpack_dense(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Storage order of the packed operand: 16-row x 64-channel tiles
+# ----------------------------------------------------------------------------
+TILE_ROWS = 16
+TILE_CHANNELS = 64
+
+
+def padded_rows(M: int) -> int:
+    """Rows of the stored packed operand: M rounded up to a multiple of 16."""
+    return -(-M // TILE_ROWS) * TILE_ROWS
+
+
+def tile_rows(rowmajor: np.ndarray, K: int, pad_value: int) -> np.ndarray:
+    """Row-major per-row data [M, K * w / 64] -> stored order.
+
+    The stored order is [ceil(M/16)][K/64][16][w]: for each block of 16 rows
+    and each 64-channel step, the 16 rows' w items of that step (w = 32 kept
+    values, or 8 metadata bytes) are contiguous, row after row.  Rows past M
+    in the last block hold pad_value.
+    """
+    M, L = rowmajor.shape
+    w = L * TILE_CHANNELS // K
+    Mp = padded_rows(M)
+    full = np.full((Mp, L), pad_value, dtype=rowmajor.dtype)
+    full[:M] = rowmajor
+    return full.reshape(Mp // 16, 16, K // 64, w).transpose(0, 2, 1, 3).copy()
+
+
+def untile_rows(stored: np.ndarray, M: int, K: int) -> np.ndarray:
+    """Inverse of tile_rows (padding dropped): -> row-major [M, K * w / 64]."""
+    nb, steps, rows, w = stored.shape
+    return stored.transpose(0, 2, 1, 3).reshape(nb * rows, steps * w)[:M]
+
+
+# ----------------------------------------------------------------------------
 # The whole sparsifier and the layer (방법론, "핵심 메커니즘"; 코드 예제)
 # ----------------------------------------------------------------------------
 @dataclass
 class SparsifyResult:
     idx: np.ndarray      # int64 [M, K/4, 2]
-    values: np.ndarray   # uint16 [M, K/2] (bf16 bits, unscaled)
-    meta: np.ndarray     # uint8 [M, K/8]
+    values: np.ndarray   # uint16 [M, K/2] (bf16 bits, unscaled), row-major
+    meta: np.ndarray     # uint8 [M, K/8], row-major
     scale: np.ndarray    # fp64 [M]
     T: np.ndarray | None  # fp64 [M, R] = X LB^T, or None without LoRA
+
+    def values_stored(self) -> np.ndarray:
+        """values in stored order, padding rows zero (flat, uint16)."""
+        K = self.values.shape[1] * 2
+        return tile_rows(self.values, K, 0).reshape(-1)
+
+    def meta_stored(self) -> np.ndarray:
+        """meta in stored order, padding rows coded (0,1),(0,1) = 0x44 (flat)."""
+        K = self.meta.shape[1] * 8
+        return tile_rows(self.meta, K, 0x44).reshape(-1)
 
 
 def sparsify(X_bits: np.ndarray, LB_bits: np.ndarray | None = None) -> SparsifyResult:

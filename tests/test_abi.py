@@ -53,7 +53,8 @@ def test_workspace_bytes():
     ws = _abi.workspace_bytes(4096, 3072, 64)
     # values M*K + meta M*K/8 + scale 4M + T 2MR, each 256-aligned
     assert ws == 4096 * 3072 + 4096 * 3072 // 8 + 4096 * 4 + 4096 * 64 * 2
-    assert _abi.workspace_bytes(3, 128, 16) == 512 + 256 + 256 + 256  # 384 B of values rounds up
+    # M = 3 -> 16 stored rows: values 16*128 B, meta 16*16 B, scale and T rounded to 256 B
+    assert _abi.workspace_bytes(3, 128, 16) == 2048 + 256 + 256 + 256
     assert _abi.workspace_bytes(16, 100, 0) == 0      # K not a multiple of 128
     assert _abi.workspace_bytes(16, 128, 8) == 0      # unsupported rank
     assert _abi.workspace_bytes(-1, 128, 0) == 0

@@ -56,10 +56,10 @@ def test_linear_packed_entry(M, K, N, R):
     ref = orc.sparsify(L.X, L.LB)
     T_bits = bf16_bits_from_f32(ref.T.astype(np.float32))
     scale = torch.from_numpy(ref.scale.astype(np.float32)).cuda()
-    meta = torch.from_numpy(ref.meta).cuda()
+    meta = torch.from_numpy(ref.meta_stored()).cuda()
     say(f"packed M={M} K={K} N={N} R={R}")
-    Y = lynx.linear_sparse_lora_packed(dev(ref.values), meta, scale, dev(T_bits), dev(L.W),
-                                       dev(L.LA))
+    Y = lynx.linear_sparse_lora_packed(dev(ref.values_stored()), meta, scale, dev(T_bits),
+                                       dev(L.W), dev(L.LA))
     torch.cuda.synchronize()
     Yref = orc.linear_from_packed(ref.values, ref.meta, ref.scale.astype(np.float32), T_bits,
                                   L.W, L.LA, K)

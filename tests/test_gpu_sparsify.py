@@ -18,19 +18,20 @@ from workloads import CONFIGS, make_activation, make_weights
 pytestmark = pytest.mark.gpu
 
 
-def check_sparsify(Xb, LBb, label, rows=None):
+def check_sparsify(Xb, LBb, label):
+    """Stored packed operand (incl. padding rows) bit-exact, scale, T."""
     M, K = Xb.shape
     say(f"sparsify {label} M={M} K={K} R={0 if LBb is None else LBb.shape[0]}")
     values, meta, scale, T = lynx.sparsify(dev(Xb), None if LBb is None else dev(LBb))
     torch.cuda.synchronize()
-    sel = slice(None) if rows is None else rows
-    ref = orc.sparsify(Xb[sel], LBb)
-    np.testing.assert_array_equal(meta.cpu().numpy()[sel], ref.meta, err_msg=f"{label}: meta")
-    np.testing.assert_array_equal(host_bits(values)[sel], ref.values, err_msg=f"{label}: values")
-    s = scale.cpu().numpy().astype(np.float64)[sel]
+    ref = orc.sparsify(Xb, LBb)
+    np.testing.assert_array_equal(meta.cpu().numpy(), ref.meta_stored(), err_msg=f"{label}: meta")
+    np.testing.assert_array_equal(host_bits(values), ref.values_stored(),
+                                  err_msg=f"{label}: values")
+    s = scale.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(s / ref.scale - 1)) <= SCALE_REL_TOL, f"{label}: scale"
     if LBb is not None:
-        Tg = host_f64(T)[sel]
+        Tg = host_f64(T)
         rep = report(f"{label} T", Tg, ref.T)
         zero = np.linalg.norm(ref.T, axis=1) == 0
         assert np.all(Tg[zero] == 0)
@@ -107,8 +108,10 @@ def test_sparsify_full_size(M, K, kind):
     values, meta, scale, T = lynx.sparsify(dev(Xb), dev(LB))
     torch.cuda.synchronize()
     idx = orc.select_top2_of_4(Xb)
-    np.testing.assert_array_equal(meta.cpu().numpy(), orc.pack_meta(idx))
-    np.testing.assert_array_equal(host_bits(values), orc.pack_values(Xb, idx))
+    np.testing.assert_array_equal(meta.cpu().numpy(),
+                                  orc.tile_rows(orc.pack_meta(idx), K, 0x44).reshape(-1))
+    np.testing.assert_array_equal(host_bits(values),
+                                  orc.tile_rows(orc.pack_values(Xb, idx), K, 0).reshape(-1))
     s_ref = orc.norm_scale(orc.decode_bf16(Xb), orc.keep_mask(idx))
     s = scale.cpu().numpy().astype(np.float64)
     assert np.max(np.abs(s / s_ref - 1)) <= SCALE_REL_TOL

@@ -303,3 +303,25 @@ def test_meta_pack_unpack_round_trip():
     codes = orc.pack_meta(idx)
     lo = codes & 0xF
     assert set(np.unique(lo).tolist()) <= {4, 8, 12, 9, 13, 14}
+
+
+# ---------------------------------------------------------------------------
+# storage order of the packed operand (tiles of 16 rows x 64 channels)
+# ---------------------------------------------------------------------------
+def test_tiled_storage_offsets_by_hand():
+    """Offsets written out from the format definition for M = 20, K = 192:
+    Mp = 32, 3 steps; value j of row m at ((m//16)*3 + j//32)*512 + (m%16)*32 + j%32,
+    meta byte j of row m at ((m//16)*3 + j//8)*128 + (m%16)*8 + j%8."""
+    M, K = 20, 192
+    vals = (np.arange(M * K // 2) % 65521).astype(np.uint16).reshape(M, K // 2)
+    meta = (np.arange(M * K // 8) % 251).astype(np.uint8).reshape(M, K // 8)
+    tv = orc.tile_rows(vals, K, 0).reshape(-1)
+    tm = orc.tile_rows(meta, K, 0x44).reshape(-1)
+    assert tv.size == 32 * K // 2 and tm.size == 32 * K // 8
+    assert tv[(1 * 3 + 1) * 512 + 1 * 32 + 8] == vals[17, 40]     # m=17, j=40
+    assert tv[(0 * 3 + 2) * 512 + 5 * 32 + 31] == vals[5, 95]     # m=5, j=95
+    assert tm[(0 * 3 + 1) * 128 + 5 * 8 + 5] == meta[5, 13]       # m=5, j=13
+    assert tm[(1 * 3 + 2) * 128 + 3 * 8 + 7] == meta[19, 23]      # m=19, j=23
+    # padding rows 20..31 of the second block: zero values, meta 0x44
+    assert tv[(1 * 3 + 0) * 512 + 4 * 32] == 0 and tm[(1 * 3 + 2) * 128 + 15 * 8] == 0x44
+    np.testing.assert_array_equal(orc.untile_rows(orc.tile_rows(vals, K, 0), M, K), vals)
