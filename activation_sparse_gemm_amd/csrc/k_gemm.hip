@@ -1,5 +1,5 @@
-// Tiled GEMM kernels for gfx950: K2 (2:4 sparse MFMA + LoRA epilogue) and K3
-// (dense MFMA baseline), sharing one tile pipeline.
+// Tiled GEMM kernels for gfx950: K2 (2:4 sparse MFMA + LoRA, gemm_sparse32)
+// and K3 (dense MFMA baseline, gemm_dense).
 //
 // Layer (RT-Lynx page, 코드 예제, second formula; 방법론 "핵심 메커니즘" and
 // "CUDA 커널 최적화": the 2:4 activation goes to the sparse unit, the LoRA
@@ -10,32 +10,24 @@
 // epilogue; T / s is rounded to bf16 once when staged (its share of Y is a few
 // per mille, so that rounding is far below the output's own bf16 rounding).
 //
-// Tiling: one 256 x 256 output tile per workgroup of 4 waves (2 x 2), each wave
-// 128 x 128 = 8 x 8 accumulator tiles of 16 x 16 (256 fp32 per lane, in AGPRs).
-// Operands move global -> LDS by buffer_load ... lds (no VGPR staging) into a
-// ring of LDS stages of 64 dense channels:
-//   sparse: A = packed values 256 x 64 B, meta 256 x 8 B, B = W 256 x 128 B
-//           (50 KB, 1024 matrix-core cycles per wave); ring of 3 (150 KB),
-//           loads issued 2 stages ahead.  The packed operand is stored in
-//           16-row x 64-channel tiles, so a stage's A side is 16 contiguous
-//           1 KB value tiles and 16 contiguous 128 B meta tiles;
-//   dense:  32 channels per stage: A = X 256 x 64 B, B = W 256 x 64 B
-//           (32 KB, 1024 cycles); ring of 4 (128 KB), loads issued 3 ahead.
-// The sparse A side is read as whole 128-byte lines, which keeps the L1 -> L2
-// request rate (about one line per clock per CU) below the matrix-core rate.
+// Both kernels: one 256 x 256 output tile per workgroup of 4 waves (2 x 2),
+// each wave 128 x 128 (256 fp32 accumulators per lane, in AGPRs).  Operands
+// move global -> LDS by buffer_load ... lds (no VGPR staging) into a ring of
+// LDS stages:
+//   sparse: 64 dense channels per stage: packed values 256 x 64 B, meta
+//           256 x 8 B, W 256 x 128 B (50 KB, 1024 matrix-core cycles per
+//           wave); ring of 3 (150 KB), loads issued 2 stages ahead.  The packed
+//           operand is stored in 16-row x 64-channel tiles, so a stage's A side
+//           is 16 contiguous 1 KB value tiles and 16 contiguous 128 B meta
+//           tiles, read as whole 128-byte lines;
+//   dense:  32 channels per stage: X 256 x 64 B, W 256 x 64 B (32 KB, 1024
+//           cycles); ring of 4 (128 KB), loads issued 3 stages ahead.
 // The loads of a stage are waited for with an explicit vmcnt that leaves the
 // later stages' loads in flight, then one s_barrier per stage.  Rows past M or
 // N lie past the end of their buffer resource and are never read (their LDS
 // slots keep stale values, which only reach outputs that are not stored).
 // LDS rows keep their 16-byte chunks XOR-swizzled by row so the fragment reads
 // of 8 (and 16) consecutive lanes hit distinct banks.
-//
-// Register layouts (pinned by the probe tests), lane l, r = l % 16, q = l / 16:
-//   v_smfmac_f32_16x16x64_bf16: A = row r, dense channels [16q, 16q+16) as 8
-//     kept values + 16-bit index word; B = column r, channel chunks q and 4+q
-//     (8 channels each) of the 64-channel step.
-//   v_mfma_f32_16x16x32_bf16: A = row r, B = column r, channels [8q, 8q+8).
-//   16 x 16 accumulator: column r, rows 4q .. 4q+3.
 //
 // Tile order: workgroups are handed to the 8 XCDs round-robin, so ids are
 // remapped to give each XCD a contiguous range of tiles, and tiles are
@@ -146,16 +138,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-template <bool SPARSE>
-__global__ __launch_bounds__(NT, 1) void gemm_tiled(
-    const uint16_t* __restrict__ Aptr,   // SPARSE: values [M][K/2]; dense: X [M][K]
-    const uint8_t* __restrict__ meta,    // SPARSE only: [M][K/8]
-    const float* __restrict__ scale,     // SPARSE only: [M]
-    const uint16_t* __restrict__ T,      // SPARSE only: [M][R] or null
-    const uint16_t* __restrict__ W,      // [N][K]
-    const uint16_t* __restrict__ LA,     // SPARSE only: [N][R] or null
-    uint16_t* __restrict__ Y, int M, int N, int K, int R) {
-    using C = Cfg<SPARSE>;
+// ---------------------------------------------------------------------------
+// K3: dense bf16 GEMM Y = X W^T with v_mfma_f32_16x16x32_bf16.
+//
+// 256 x 256 tile per workgroup of 4 waves (2 x 2, 128 x 128 each = 8 x 8
+// accumulator tiles of 16 x 16); ring of 4 LDS stages of 32 channels (X and W
+// 256 x 64 B each, swizzled 64-byte rows), loads issued 3 stages ahead.
+// Lane l, r = l % 16, q = l / 16: A = row r, B = column r, channels
+// [8q, 8q+8) of the stage; accumulator = column r, rows 4q .. 4q+3.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT, 1) void gemm_dense(const uint16_t* __restrict__ X,
+                                                     const uint16_t* __restrict__ W,
+                                                     uint16_t* __restrict__ Y, int M, int N,
+                                                     int K) {
+    using C = Cfg<false>;
     __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
 
     const int tid = threadIdx.x;
@@ -169,74 +165,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
     tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
 
-    // ---- DMA addressing --------------------------------------------------
-    // sparse A: instruction j of wave w moves the 1 KB value tile of row block
-    //   (m0/16 + w + 4j) into LDS rows 16 (w + 4j) .. +16 (64 B each);
-    // sparse meta (dword DMA, 256 B): the two 128 B tiles of row blocks
-    //   2 (w + 4j), 2 (w + 4j) + 1 into LDS rows 32 (w + 4j) .. +32 (8 B each);
-    // sparse W (128-byte LDS rows): instruction j moves rows 8 (w + 4j) + l/8;
-    // dense X and W (64-byte LDS rows): instruction j moves rows 16 (w + 4j) + l/4.
-    // Lane l lands at LDS byte 16 l (4 l) of the instruction's 1 KB (256 B);
-    // its source is the chunk the row's swizzle puts there.
+    // ---- DMA addressing: instruction j of wave w moves rows 16 (w + 4j) + l/4
+    // of the stage (64-byte LDS rows); lane l lands at LDS byte 16 l of the
+    // instruction's 1 KB, its source is the chunk the row's swizzle puts there.
     const uint32_t lds0 = static_cast<uint32_t>(
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
-    const int steps = K / 64;
-    const int Mp = (M + 15) & ~15;
-    const i32x4 rsA = SPARSE ? make_rsrc(Aptr, uint32_t(Mp) * uint32_t(K))
-                             : make_rsrc(Aptr, uint32_t(M) * uint32_t(2 * K));
+    const i32x4 rsA = make_rsrc(X, uint32_t(M) * uint32_t(2 * K));
     const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
-    i32x4 rsM = {0, 0, 0, 0};
-    if constexpr (SPARSE) rsM = make_rsrc(meta, uint32_t(Mp) * uint32_t(K / 8));
-
-    int voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA > 0 ? C::M_DMA : 1];
+    int voffA[C::A_DMA], voffB[C::B_DMA];
 #pragma unroll
     for (int j = 0; j < C::A_DMA; ++j) {
-        if constexpr (SPARSE) {
-            const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
-            voffA[j] = (m0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
-        } else {
-            const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
-            voffA[j] = (m0 + row) * 2 * K + 16 * (ph ^ swz64(row));
-        }
+        const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
+        voffA[j] = (m0 + row) * 2 * K + 16 * (ph ^ swz64(row));
     }
 #pragma unroll
     for (int j = 0; j < C::B_DMA; ++j) {
-        if constexpr (SPARSE) {
-            const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
-            voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz128(row));
-        } else {
-            const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
-            voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz64(row));
-        }
-    }
-    if constexpr (SPARSE) {
-#pragma unroll
-        for (int j = 0; j < C::M_DMA; ++j) {
-            const int blk = 2 * (wave + 4 * j) + (lane >> 5);
-            voffM[j] = (m0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
-        }
+        const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
+        voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz64(row));
     }
 
-    // loads of k-stage t into ring slot t % NSTAGE (k offsets in bytes)
+    // loads of k-stage t into ring slot t % NSTAGE
     auto issue_stage = [&](int t) {
         const uint32_t base = lds0 + uint32_t((t % C::NSTAGE) * C::STAGE);
-        const int kA = SPARSE ? t * 1024 : t * 64;
 #pragma unroll
-        for (int j = 0; j < C::A_DMA; ++j) dma16(base + 1024 * (wave + 4 * j), voffA[j], rsA, kA);
-        if constexpr (SPARSE) {
-#pragma unroll
-            for (int j = 0; j < C::M_DMA; ++j)
-                dma4(base + C::A_BYTES + 256 * (wave + 4 * j), voffM[j], rsM, t * 128);
-        }
+        for (int j = 0; j < C::A_DMA; ++j) dma16(base + 1024 * (wave + 4 * j), voffA[j], rsA, t * 64);
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j)
-            dma16(base + C::A_BYTES + C::META_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB,
-                  t * C::B_ROW);
+            dma16(base + C::A_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB, t * 64);
     };
 
-    // ---- per-lane fragment offsets (swizzle depends on row % 16 = r only) --
-    const int s64 = swz64(r), s128 = swz128(r);
-    (void)s64;
+    const int s64 = swz64(r);
     const int rowA = wm * 128 + r, rowB = wn * 128 + r;
 
     f32x4 acc[8][8];
@@ -247,11 +205,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
 
     const int nk = K / C::BK;
     __builtin_amdgcn_s_waitcnt(0);
-    if constexpr (SPARSE) {
-        // s of the tile's 256 rows into LDS (rows past M repeat the last row)
-        reinterpret_cast<float*>(smem + C::SCALE_OFF)[tid] = scale[min(m0 + tid, M - 1)];
-    }
-
     // prologue: NSTAGE - 1 stages in flight
 #pragma unroll
     for (int t = 0; t < C::NSTAGE - 1; ++t)
@@ -265,52 +218,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
 
     for (int t = 0; t < nk; ++t) {
         if (t + C::NSTAGE - 1 < nk) issue_stage(t + C::NSTAGE - 1);
-        const char* cur = smem + (t % C::NSTAGE) * C::STAGE;
-        if constexpr (SPARSE) {
-            const char* As = cur;
-            const char* Ms = cur + C::A_BYTES;
-            const char* Bs = cur + C::A_BYTES + C::META_BYTES;
-            bf16x16 bfr[8];
+        const char* As = smem + (t % C::NSTAGE) * C::STAGE;
+        const char* Bs = As + C::A_BYTES;
+        bf16x8 bfr[8];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int base = (rowB + 16 * b) * 128;
-                const bf16x8 lo = lds_read<bf16x8>(Bs, base + 16 * (q ^ s128));
-                const bf16x8 hi = lds_read<bf16x8>(Bs, base + 16 * ((4 + q) ^ s128));
-                bfr[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
-                                                 12, 13, 14, 15);
-            }
+        for (int b = 0; b < 8; ++b)
+            bfr[b] = lds_read<bf16x8>(Bs, (rowB + 16 * b) * 64 + 16 * (q ^ s64));
 #pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                const int row = rowA + 16 * a;
-                const bf16x8 afr = lds_read<bf16x8>(As, row * 64 + 16 * (q ^ s64));
-                const int idx = lds_read<uint16_t>(Ms, row * 8 + 2 * q);
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    acc[a][b] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(afr, bfr[b], acc[a][b],
-                                                                          idx, 0, 0);
-            }
-        } else {
-            const char* As = cur;
-            const char* Bs = cur + C::A_BYTES;
-            bf16x8 bfr[8];
+        for (int a = 0; a < 8; ++a) {
+            const bf16x8 afr = lds_read<bf16x8>(As, (rowA + 16 * a) * 64 + 16 * (q ^ s64));
 #pragma unroll
             for (int b = 0; b < 8; ++b)
-                bfr[b] = lds_read<bf16x8>(Bs, (rowB + 16 * b) * 64 + 16 * (q ^ s64));
-#pragma unroll
-            for (int a = 0; a < 8; ++a) {
-                const bf16x8 afr = lds_read<bf16x8>(As, (rowA + 16 * a) * 64 + 16 * (q ^ s64));
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b], 0,
-                                                                        0, 0);
-            }
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b], 0, 0, 0);
         }
         if (t + 1 < nk) {
             // wait for stage t+1; the stages issued after it may stay in flight
             const int later = min(nk - 2 - t, C::NSTAGE - 2);
             if (later == C::NSTAGE - 2) {
                 wait_vmcnt<(C::NSTAGE - 2) * C::DMA_PER_STAGE>();
-            } else if (C::NSTAGE == 4 && later == 1) {
+            } else if (later == 1) {
                 wait_vmcnt<C::DMA_PER_STAGE>();
             } else {
                 __builtin_amdgcn_s_waitcnt(0);
@@ -321,74 +247,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // all waves done with the ring before LDS is reused
 
-    // ---- LoRA up-projection: acc += (T / s) LA^T  ----------------------------
-    if constexpr (SPARSE) {
-        if (R > 0) {
-            // T / s (rows m0..) and LA (rows n0..), 256 x 64 bf16 each, zero past
-            // R, in swizzled 128-byte rows.  All loads are issued before any is
-            // used (clamped in-bounds addresses; out-of-range chunks are zeroed).
-            char* Ts = smem;
-            char* Ls = smem + 32 * 1024;
-            const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
-            u32x4 traw[8], lraw[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = tid + NT * j;
-                const int row = c >> 3, kc = min(8 * (c & 7), R - 8);
-                traw[j] = *reinterpret_cast<const u32x4*>(T + size_t(min(m0 + row, M - 1)) * R + kc);
-                lraw[j] = *reinterpret_cast<const u32x4*>(LA + size_t(min(n0 + row, N - 1)) * R + kc);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int c = tid + NT * j;
-                const int row = c >> 3, ch = c & 7;
-                const int off = row * 128 + 16 * (ch ^ swz128(row));
-                const bool live = 8 * ch < R;
-                const float inv = 1.0f / s_lds[row];
-                const u32x4 raw = traw[j];
-                u32x4 tv;
-                tv.x = pack_bf16x2(bf16_lo(raw.x) * inv, bf16_hi(raw.x) * inv);
-                tv.y = pack_bf16x2(bf16_lo(raw.y) * inv, bf16_hi(raw.y) * inv);
-                tv.z = pack_bf16x2(bf16_lo(raw.z) * inv, bf16_hi(raw.z) * inv);
-                tv.w = pack_bf16x2(bf16_lo(raw.w) * inv, bf16_hi(raw.w) * inv);
-                const u32x4 zero = {0u, 0u, 0u, 0u};
-                *reinterpret_cast<u32x4*>(Ts + off) = live ? tv : zero;
-                *reinterpret_cast<u32x4*>(Ls + off) = live ? lraw[j] : zero;
-            }
-            __syncthreads();
-            for (int ks = 0; ks < (R + 31) / 32; ++ks) {
-                bf16x8 bfr[8];
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    bfr[b] = lds_read<bf16x8>(Ls, (rowB + 16 * b) * 128 + 16 * ((4 * ks + q) ^ s128));
-#pragma unroll
-                for (int a = 0; a < 8; ++a) {
-                    const bf16x8 afr =
-                        lds_read<bf16x8>(Ts, (rowA + 16 * a) * 128 + 16 * ((4 * ks + q) ^ s128));
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b],
-                                                                            0, 0, 0);
-                }
-            }
-        }
-    }
-
-    // ---- epilogue: y = s * acc (sparse) or acc (dense), bf16, via LDS --------
+    // ---- epilogue: bf16 through LDS, 16 rows at a time, 16-byte stores ------
     char* ep = smem + C::EPI_OFF + wave * 4096;  // 16 rows x 128 cols bf16
     const bool vec_ok = (N & 7) == 0;
 #pragma unroll
     for (int a = 0; a < 8; ++a) {
-        const int row_l = 16 * a + 4 * q;  // row within the wave tile of element e = 0
-        f32x4 s4 = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (SPARSE)
-            s4 = *reinterpret_cast<const f32x4*>(smem + C::SCALE_OFF + 4 * (wm * 128 + row_l));
 #pragma unroll
         for (int b = 0; b < 8; ++b)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 *reinterpret_cast<uint16_t*>(ep + (4 * q + e) * 256 + (16 * b + r) * 2) =
-                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(s4[e] * acc[a][b][e]));
+                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][e]));
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -417,6 +286,304 @@ __global__ __launch_bounds__(NT, 1) void gemm_tiled(
     }
 }
 
+// ---------------------------------------------------------------------------
+// K2: Y = s * (X~ W^T + (T / s) LA^T) with v_smfmac_f32_32x32x32_bf16.
+//
+// Each wave's 128 x 128 is 4 x 4 accumulator tiles of 32 x 32 (16 fp32 each).
+// A stage is two 32-channel sub-steps of 16 SMFMACs (32 cycles each).  The
+// fragments of one sub-step take 52 VGPRs (A: 4 x (8 values + index word),
+// B: 4 x 16 values), so two sets fit beside the accumulators and alternate by
+// sub-step.  Every DMA and LDS read is issued between two SMFMACs (order pinned
+// by sched_barrier), so the matrix core keeps issuing while they are queued.
+//
+// Lane l, r = l % 32, h = l / 32 (layouts pinned by the probe tests):
+//   A = row r, dense channels [16h, 16h+16) of the 32-channel sub-step: 8 kept
+//     values (chunk 2 sub + h of the 64-byte LDS row) + 16-bit index word;
+//   B = column r, channels [8h, 8h+8) and [16+8h, 24+8h): chunks 4 sub + h and
+//     4 sub + 2 + h of the 128-byte LDS row;
+//   D = column r, rows 8 (e / 4) + 4 h + e % 4, e = 0..15.
+// The LoRA up-projection runs on the same instruction (see the epilogue).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT, 1) void gemm_sparse32(
+    const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta,
+    const float* __restrict__ scale, const uint16_t* __restrict__ T,
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ LA,
+    uint16_t* __restrict__ Y, int M, int N, int K, int R) {
+    using C = Cfg<true>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, h = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;
+
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+
+    // ---- DMA addressing ----------------------------------------------------
+    // values: instruction j of wave w moves the 1 KB value tile of row block
+    //   (m0/16 + w + 4j) into LDS rows 16 (w + 4j) .. +16 (64 B each);
+    // meta (dword DMA, 256 B): the two 128 B tiles of row blocks 2 (w + 4j)
+    //   and 2 (w + 4j) + 1 into LDS rows 32 (w + 4j) .. +32 (8 B each);
+    // W (128-byte LDS rows): instruction j moves rows 8 (w + 4j) + l/8.
+    // Lane l lands at LDS byte 16 l (4 l) of the instruction's 1 KB (256 B);
+    // its source is the chunk the row's swizzle puts there.
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+    const int steps = K / 64;
+    const int Mp = (M + 15) & ~15;
+    const i32x4 rsA = make_rsrc(values, uint32_t(Mp) * uint32_t(K));
+    const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
+    const i32x4 rsM = make_rsrc(meta, uint32_t(Mp) * uint32_t(K / 8));
+    int voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA];
+#pragma unroll
+    for (int j = 0; j < C::A_DMA; ++j) {
+        const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
+        voffA[j] = (m0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
+    }
+#pragma unroll
+    for (int j = 0; j < C::B_DMA; ++j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
+        voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz128(row));
+    }
+#pragma unroll
+    for (int j = 0; j < C::M_DMA; ++j) {
+        const int blk = 2 * (wave + 4 * j) + (lane >> 5);
+        voffM[j] = (m0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
+    }
+    // one of the 14 DMA instructions of a stage (4 value tiles, 2 meta, 8 W)
+    auto dma_k = [&](int t, uint32_t slot_off, int k) {
+        const uint32_t base = lds0 + slot_off;
+        if (k < C::A_DMA) {
+            dma16(base + 1024 * (wave + 4 * k), voffA[k], rsA, t * 1024);
+        } else if (k < C::A_DMA + C::M_DMA) {
+            const int j = k - C::A_DMA;
+            dma4(base + C::A_BYTES + 256 * (wave + 4 * j), voffM[j], rsM, t * 128);
+        } else {
+            const int j = k - C::A_DMA - C::M_DMA;
+            dma16(base + C::A_BYTES + C::META_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB, t * 128);
+        }
+    };
+
+    // ---- fragments ---------------------------------------------------------
+    const int s64 = swz64(r), s128 = swz128(r);
+    const int offA = (wm * 128 + r) * 64;      // + 32 a rows (a * 2048 bytes)
+    const int offM = (wm * 128 + r) * 8;       // + a * 256
+    const int offB = (wn * 128 + r) * 128;     // + b * 4096
+    struct Frags {
+        bf16x8 a[4];
+        int i[4];
+        bf16x8 blo[4], bhi[4];
+    };
+    // one of the 16 LDS reads of a fragment set: k < 8 -> A value / index of
+    // row block k / 2, k >= 8 -> low / high half of B column block (k - 8) / 2
+    auto lds_k = [&](int slot, int sub, Frags& f, int k) {
+        const char* As = smem + slot * C::STAGE;
+        const char* Ms = As + C::A_BYTES;
+        const char* Bs = Ms + C::META_BYTES;
+        if (k < 8) {
+            const int a = k >> 1;
+            if ((k & 1) == 0)
+                f.a[a] = lds_read<bf16x8>(As, offA + a * 2048 + 16 * ((2 * sub + h) ^ s64));
+            else
+                f.i[a] = lds_read<uint16_t>(Ms, offM + a * 256 + 2 * (2 * sub + h));
+        } else {
+            const int b = (k - 8) >> 1;
+            if ((k & 1) == 0)
+                f.blo[b] = lds_read<bf16x8>(Bs, offB + b * 4096 + 16 * ((4 * sub + h) ^ s128));
+            else
+                f.bhi[b] = lds_read<bf16x8>(Bs, offB + b * 4096 + 16 * ((4 * sub + 2 + h) ^ s128));
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+    // SMFMAC k of a sub-step: tile (k / 4, k % 4)
+    auto mma_k = [&](const Frags& f, int k) {
+        const int a = k >> 2, b = k & 3;
+        const bf16x16 bv = __builtin_shufflevector(f.blo[b], f.bhi[b], 0, 1, 2, 3, 4, 5, 6, 7, 8,
+                                                   9, 10, 11, 12, 13, 14, 15);
+        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[a], bv, acc[a][b], f.i[a], 0, 0);
+    };
+
+    // s of the tile's 256 rows into LDS (rows past M repeat the last row)
+    reinterpret_cast<float*>(smem + C::SCALE_OFF)[tid] = scale[min(m0 + tid, M - 1)];
+
+    // Main loop, per stage t (fragment set 0 of stage t already in registers):
+    //   sub-step 0: 16 SMFMACs on set 0, each followed by one DMA instruction of
+    //     stage t+2 (into slot (t+2) % 3, freed by the previous barrier) and one
+    //     LDS read of set 1 (same slot as set 0);
+    //   sub-step 1: 8 SMFMACs on set 1; wait for stage t+1's loads and this
+    //     wave's reads; barrier; 8 SMFMACs each followed by two LDS reads of
+    //     stage t+1's set 0.
+    // Every memory instruction sits between two SMFMACs, so the matrix core
+    // keeps issuing while they are queued; the order is pinned with
+    // sched_barrier.
+    const int nk = K / 64;  // even: K is a multiple of 128
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, 0, k);
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, C::STAGE, k);
+    wait_vmcnt<C::DMA_PER_STAGE>();
+    block_barrier();
+    Frags f0, f1;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) lds_k(0, 0, f0, k);
+    // The last two stages load stage nk - 1 once more into the free slot
+    // instead of branching around the loads: every stage body is the same
+    // straight-line code.  The copies are never read and have landed before
+    // LDS is reused.
+    for (int t = 0; t < nk; ++t) {
+        const int slot = t % 3;
+        const int tl = min(t + 2, nk - 1);
+        const uint32_t lslot = uint32_t(((t + 2) % 3) * C::STAGE);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            mma_k(f0, k);
+            if (k < C::DMA_PER_STAGE) dma_k(tl, lslot, k);
+            lds_k(slot, 1, f1, k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            mma_k(f1, k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();  // stage t + 1 has landed
+        block_barrier();
+        const int nslot = (t + 1) % 3;  // stale after the last stage, never used
+#pragma unroll
+        for (int k = 8; k < 16; ++k) {
+            mma_k(f1, k);
+            lds_k(nslot, 0, f0, 2 * (k - 8));
+            lds_k(nslot, 0, f0, 2 * (k - 8) + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // all waves done with the ring before LDS is reused
+
+    const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
+    // ---- LoRA up-projection: acc += (T / s) LA^T ----------------------------
+    if (R > 0) {
+        char* Ts = smem;
+        char* Ls = smem + 32 * 1024;
+        u32x4 traw[8], lraw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = tid + NT * j;
+            const int row = c >> 3, kc = min(8 * (c & 7), R - 8);
+            traw[j] = *reinterpret_cast<const u32x4*>(T + size_t(min(m0 + row, M - 1)) * R + kc);
+            lraw[j] = *reinterpret_cast<const u32x4*>(LA + size_t(min(n0 + row, N - 1)) * R + kc);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = tid + NT * j;
+            const int row = c >> 3, ch = c & 7;
+            const int off = row * 128 + 16 * (ch ^ swz128(row));
+            const bool live = 8 * ch < R;
+            const float inv = 1.0f / s_lds[row];
+            const u32x4 raw = traw[j];
+            u32x4 tv;
+            tv.x = pack_bf16x2(bf16_lo(raw.x) * inv, bf16_hi(raw.x) * inv);
+            tv.y = pack_bf16x2(bf16_lo(raw.y) * inv, bf16_hi(raw.y) * inv);
+            tv.z = pack_bf16x2(bf16_lo(raw.z) * inv, bf16_hi(raw.z) * inv);
+            tv.w = pack_bf16x2(bf16_lo(raw.w) * inv, bf16_hi(raw.w) * inv);
+            const u32x4 zero = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Ts + off) = live ? tv : zero;
+            *reinterpret_cast<u32x4*>(Ls + off) = live ? lraw[j] : zero;
+        }
+        __syncthreads();
+        // T / s is dense; it is fed to the same SMFMAC as two exactly-2:4 halves
+        // with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per group):
+        // over channels [16h, 16h+16) of a 32-rank step the even dwords of the
+        // row are positions 0,1 of each group and the odd dwords positions 2,3.
+        // LA supplies the B operand exactly as W does in the main loop.
+        for (int ks = 0; ks < (R + 31) / 32; ++ks) {
+            const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
+            const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128), ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
+            bf16x16 bl[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const int row = (wn * 128 + 32 * b + r) * 128;
+                const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
+                const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
+                bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
+                                                14, 15);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const int row = (wm * 128 + 32 * a + r) * 128;
+                const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
+                const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
+                const bf16x8 te = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.z, t1.x, t1.z});
+                const bf16x8 to = __builtin_bit_cast(bf16x8, u32x4{t0.y, t0.w, t1.y, t1.w});
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(te, bl[b], acc[a][b],
+                                                                          0x4444, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(to, bl[b], acc[a][b],
+                                                                          0xEEEE, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: y = s * acc, bf16, 16 rows at a time through LDS ---------
+    // rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4; the
+    // half p = 0 / 1 (e < 8 / e >= 8) covers rows 0..15 / 16..31.
+    char* ep = smem + C::EPI_OFF + wave * 4096;  // 16 rows x 128 cols bf16
+    const bool vec_ok = (N & 7) == 0;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int rbase = wm * 128 + 32 * a + 16 * p;  // tile row of local row 0
+            const f32x4 sA = *reinterpret_cast<const f32x4*>(s_lds + rbase + 4 * h);
+            const f32x4 sB = *reinterpret_cast<const f32x4*>(s_lds + rbase + 8 + 4 * h);
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    const int lr = 8 * (e2 / 4) + 4 * h + (e2 % 4);  // local row 0..15
+                    const float sv = e2 < 4 ? sA[e2 % 4] : sB[e2 % 4];
+                    *reinterpret_cast<uint16_t*>(ep + lr * 256 + (32 * b + r) * 2) =
+                        __builtin_bit_cast(uint16_t,
+                                           static_cast<__bf16>(sv * acc[a][b][8 * p + e2]));
+                }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int orow = m0 + rbase + (lane >> 2);
+            const int ocol = n0 + wn * 128 + (lane & 3) * 32;
+            if (orow < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const u32x4 v = lds_read<u32x4>(ep, (lane >> 2) * 256 + (lane & 3) * 64 + 16 * i);
+                    const int col = ocol + 8 * i;
+                    uint16_t* dst = Y + size_t(orow) * size_t(N) + col;
+                    if (vec_ok && col + 8 <= N) {
+                        *reinterpret_cast<u32x4*>(dst) = v;
+                    } else {
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int q2 = 0; q2 < 8; ++q2)
+                            if (col + q2 < N) dst[q2] = uint16_t(w[q2 >> 1] >> (16 * (q2 & 1)));
+                    }
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+    }
+}
+
 }  // namespace
 
 lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta,
@@ -424,16 +591,15 @@ lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta
                                      const uint16_t* LA, uint16_t* Y, int M, int N, int K, int R,
                                      hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_tiled<true>, dim3(tiles), dim3(NT), 0, stream, values, meta, scale, T,
-                       W, LA, Y, M, N, K, R);
+    hipLaunchKernelGGL(gemm_sparse32, dim3(tiles), dim3(NT), 0, stream, values, meta, scale, T, W,
+                       LA, Y, M, N, K, R);
     return launch_status();
 }
 
 lynx_status launch_gemm_dense_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                     int N, int K, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_tiled<false>, dim3(tiles), dim3(NT), 0, stream, X, nullptr, nullptr,
-                       nullptr, W, nullptr, Y, M, N, K, 0);
+    hipLaunchKernelGGL(gemm_dense, dim3(tiles), dim3(NT), 0, stream, X, W, Y, M, N, K);
     return launch_status();
 }
 

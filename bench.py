@@ -194,7 +194,7 @@ def main():
         "dense_ms": round(ms_dense, 5),
         "split_ms": {"sparsify": round(ms_k1, 5), "sparse_gemm_lora": round(ms_gemm, 5)},
         "torch_matmul_ms": round(ms_torch, 5),
-        "roofline": {"bound": "mfma", "kernel": "gemm_tiled<sparse> (2:4 SMFMAC + LoRA epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_sparse32 (2:4 SMFMAC + LoRA up-projection)",
                      "achieved": round(k2_tflops, 2), "peak": PEAK_DENSE_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k2_tflops / PEAK_DENSE_BF16_TFLOPS, 4),
                      "traffic": traffic},
