@@ -40,6 +40,12 @@ def parse():
     p.add_argument("--workload", default="mlp_up", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--sets", type=int, default=3)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after timing, run a plain 256 MiB streaming kernel (torch.neg) three "
+                        "times, the reference for HBM byte counters")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
+                        "--copy-calibration run into profiles/traffic_<workload>.json")
     return p.parse_args()
 
 
@@ -59,9 +65,12 @@ def time_region(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps
 
 
-def cpu_baseline(L, target_s=15.0):
-    """The fp64 oracle on a bounded sample of rows of the same workload."""
-    import numpy as np
+def cpu_baseline(L, min_s=10.0, max_rows_growth=8.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload.
+
+    The row count grows until one call takes about four seconds or covers the
+    whole layer; calls at that size then repeat until min_s seconds of CPU work
+    have been timed.  Each call includes the oracle's own decode of W, LA, LB."""
     from oracle import lynx_oracle as orc
     try:
         import threadpoolctl
@@ -69,20 +78,91 @@ def cpu_baseline(L, target_s=15.0):
         cores = max((i.get("num_threads", 1) for i in info), default=os.cpu_count())
     except Exception:  # pragma: no cover
         cores = os.cpu_count()
-    rows = 64
-    t0 = time.perf_counter()
-    orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
-    dt = time.perf_counter() - t0
-    # grow the sample to roughly target_s seconds of CPU work
-    rows = int(min(L.M, max(rows, rows * target_s / max(dt, 1e-3) * 0.8)))
-    t0 = time.perf_counter()
-    orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
-    dt = time.perf_counter() - t0
-    flops = 2 * rows * L.N * L.K + 2 * rows * L.R * (L.K + L.N)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s (dense-equivalent)", "cores": cores,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {rows} of {L.M} rows of the same {L.name} layer (full W, LA, LB), "
-                      f"fp64 NumPy oracle incl. selection, norms, and both contractions"}
+
+    def run(rows):
+        t0 = time.perf_counter()
+        orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
+        return time.perf_counter() - t0
+
+    rows = min(L.M, 128)
+    dt = run(rows)
+    while dt < 4.0 and rows < L.M:
+        rows = min(L.M, int(rows * min(max_rows_growth, max(2.0, 4.0 / max(dt, 1e-3)))))
+        dt = run(rows)
+    total, calls = 0.0, 0
+    while total < min_s:
+        total += run(rows)
+        calls += 1
+    flops = calls * (2 * rows * L.N * L.K + 2 * rows * L.R * (L.K + L.N))
+    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
+            "cores": cores, "kind": "oracle", "seconds": round(total, 2),
+            "sample": f"{calls} call(s) on the first {rows} of {L.M} rows of the {L.name} layer "
+                      f"(full W, LA, LB): fp64 NumPy oracle with selection, norms and both "
+                      f"contractions"}
+
+
+K2_SRC = os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc", "k_gemm.hip")
+COPY_MIB = 256
+
+
+def source_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def per_dispatch_kib(run_dir: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch, by kernel name, from rocprofv3
+    output under run_dir (rocpd SQLite database or counter_collection.csv)."""
+    import csv
+    import glob
+    import sqlite3
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*_results.db"), recursive=True):
+        con = sqlite3.connect(path)
+        for name, value in con.execute(
+                "select kernel_name, value from counters_collection where counter_name = ?",
+                (counter,)):
+            vals.setdefault(name, []).append(float(value))
+        con.close()
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
+    """HBM bytes per K2 launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for the plain streaming kernel
+    of known size (reads COPY_MIB MiB, writes COPY_MIB MiB)."""
+    fetch = per_dispatch_kib(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch_kib(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = [k for k in d if key in k]
+        if len(hits) != 1:
+            raise SystemExit(f"expected one kernel matching {key!r}, found {hits}")
+        return d[hits[0]]
+
+    known_kib = COPY_MIB * 1024.0
+    f_factor = known_kib / pick(fetch, "neg")
+    w_factor = known_kib / pick(write, "neg")
+    f_bytes = pick(fetch, "gemm_sparse32") * 1024.0 * f_factor
+    w_bytes = pick(write, "gemm_sparse32") * 1024.0 * w_factor
+    rec = {"workload": workload, "kernel": "gemm_sparse32", "kernel_sha": source_sha(K2_SRC),
+           "fetch_bytes_per_launch": round(f_bytes), "write_bytes_per_launch": round(w_bytes),
+           "bytes_per_launch": round(f_bytes + w_bytes),
+           "copy_factor_fetch": round(f_factor, 4), "copy_factor_write": round(w_factor, 4),
+           "commands": [f"rocprofv3 --pmc {c} -d <dir> -o run -- python3 bench.py --steps 3 "
+                        f"--warmup 1 --no-cpu --sets 1 --copy-calibration --workload {workload}"
+                        for c in ("FETCH_SIZE", "WRITE_SIZE")],
+           "raw_kib_per_dispatch": {"fetch": {k[:60]: round(v, 1) for k, v in fetch.items()},
+                                    "write": {k[:60]: round(v, 1) for k, v in write.items()}}}
+    out = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
 
 
 def traffic_for(kernel_src: str, workload: str):
@@ -92,13 +172,14 @@ def traffic_for(kernel_src: str, workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    with open(kernel_src, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()[:16]
-    return rec.get("bytes_per_launch") if rec.get("kernel_sha") == h else None
+    return rec.get("bytes_per_launch") if rec.get("kernel_sha") == source_sha(kernel_src) else None
 
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        print(json.dumps(summarize_traffic(*args.summarize_traffic, args.workload)))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the layer shards by rows with no communication; see the design notes)",
@@ -166,8 +247,14 @@ def main():
     # (M N K/2 multiply-adds) + LoRA up-projection (M R N multiply-adds)
     k2_alg_flops = M * N * K + 2 * M * R * N
     k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
-    traffic = traffic_for(os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc", "k_gemm.hip"),
-                          args.workload)
+    traffic = traffic_for(K2_SRC, args.workload)
+    if args.copy_calibration:
+        src = torch.ones(COPY_MIB << 19, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None if args.no_cpu else cpu_baseline(base)
 
     rec = {
