@@ -369,33 +369,40 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     };
 
     // ---- fragments ---------------------------------------------------------
+    // Two fragment sets (one per 32-channel sub-step) alternate.  SMFMACs run
+    // column-block-major, k = 4 b + a, and a set's 16 LDS reads are issued in
+    // the order that consumes them: A0, B0, A1, A2, A3, B1, B2, B3.
     const int s64 = swz64(r), s128 = swz128(r);
     const int offA = (wm * 128 + r) * 64;      // + 32 a rows (a * 2048 bytes)
     const int offM = (wm * 128 + r) * 8;       // + a * 256
     const int offB = (wn * 128 + r) * 128;     // + b * 4096
     struct Frags {
-        bf16x8 a[4];
+        bf16x8 v[4];
         int i[4];
         bf16x8 blo[4], bhi[4];
     };
-    // one of the 16 LDS reads of a fragment set: k < 8 -> A value / index of
-    // row block k / 2, k >= 8 -> low / high half of B column block (k - 8) / 2
-    auto lds_k = [&](int slot, int sub, Frags& f, int k) {
-        const char* As = smem + slot * C::STAGE;
-        const char* Ms = As + C::A_BYTES;
-        const char* Bs = Ms + C::META_BYTES;
-        if (k < 8) {
-            const int a = k >> 1;
-            if ((k & 1) == 0)
-                f.a[a] = lds_read<bf16x8>(As, offA + a * 2048 + 16 * ((2 * sub + h) ^ s64));
-            else
-                f.i[a] = lds_read<uint16_t>(Ms, offM + a * 256 + 2 * (2 * sub + h));
-        } else {
-            const int b = (k - 8) >> 1;
-            if ((k & 1) == 0)
-                f.blo[b] = lds_read<bf16x8>(Bs, offB + b * 4096 + 16 * ((4 * sub + h) ^ s128));
-            else
-                f.bhi[b] = lds_read<bf16x8>(Bs, offB + b * 4096 + 16 * ((4 * sub + 2 + h) ^ s128));
+    Frags fr[2];
+    // read n (0..15) of a set, from the ring slot at byte offset soff
+    auto read_n = [&](int soff, int sub, Frags& f, int n) {
+        const char* As = smem + soff;
+        const char* Bs = As + C::A_BYTES + C::META_BYTES;
+        // n -> (A row block, values / index) or (B column block, low / high half)
+        constexpr int kind[16] = {0, 1, 2, 3, 0, 1, 0, 1, 0, 1, 2, 3, 2, 3, 2, 3};
+        constexpr int blk[16] = {0, 0, 0, 0, 1, 1, 2, 2, 3, 3, 1, 1, 2, 2, 3, 3};
+        const int x = blk[n];
+        switch (kind[n]) {
+            case 0:
+                f.v[x] = lds_read<bf16x8>(As, offA + x * 2048 + 16 * ((2 * sub + h) ^ s64));
+                break;
+            case 1:
+                f.i[x] = lds_read<uint16_t>(As + C::A_BYTES, offM + x * 256 + 2 * (2 * sub + h));
+                break;
+            case 2:
+                f.blo[x] = lds_read<bf16x8>(Bs, offB + x * 4096 + 16 * ((4 * sub + h) ^ s128));
+                break;
+            default:
+                f.bhi[x] = lds_read<bf16x8>(Bs, offB + x * 4096 + 16 * ((4 * sub + 2 + h) ^ s128));
+                break;
         }
     };
 
@@ -404,66 +411,84 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
-    // SMFMAC k of a sub-step: tile (k / 4, k % 4)
-    auto mma_k = [&](const Frags& f, int k) {
-        const int a = k >> 2, b = k & 3;
+    auto mma = [&](const Frags& f, int k) {
+        const int a = k & 3, b = k >> 2;
         const bf16x16 bv = __builtin_shufflevector(f.blo[b], f.bhi[b], 0, 1, 2, 3, 4, 5, 6, 7, 8,
                                                    9, 10, 11, 12, 13, 14, 15);
-        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.a[a], bv, acc[a][b], f.i[a], 0, 0);
+        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.v[a], bv, acc[a][b], f.i[a], 0, 0);
     };
 
     // s of the tile's 256 rows into LDS (rows past M repeat the last row)
     reinterpret_cast<float*>(smem + C::SCALE_OFF)[tid] = scale[min(m0 + tid, M - 1)];
 
-    // Main loop, per stage t (fragment set 0 of stage t already in registers):
-    //   sub-step 0: 16 SMFMACs on set 0, each followed by one DMA instruction of
-    //     stage t+2 (into slot (t+2) % 3, freed by the previous barrier) and one
-    //     LDS read of set 1 (same slot as set 0);
-    //   sub-step 1: 8 SMFMACs on set 1; wait for stage t+1's loads and this
-    //     wave's reads; barrier; 8 SMFMACs each followed by two LDS reads of
-    //     stage t+1's set 0.
-    // Every memory instruction sits between two SMFMACs, so the matrix core
-    // keeps issuing while they are queued; the order is pinned with
-    // sched_barrier.
+    // Ring schedule.  Stage u's 14 DMA instructions go out in two halves: the
+    // first 7 in stage u - 3's sub-step 1, right after the barrier that frees
+    // slot u % 3, and the other 7 in stage u - 2's sub-step 0.  Per stage t
+    // (slot t % 3; set 0 holds sub-step 0's fragments):
+    //   sub-step 0: 16 SMFMACs on set 0; two reads of set 1 (same slot) after
+    //     each of the first 8, one DMA of stage t + 2's second half after each
+    //     of the next 7;
+    //   sub-step 1: 4 SMFMACs on set 1; wait for stage t + 1's loads and this
+    //     wave's reads; barrier (slot t % 3 is free); 12 SMFMACs, the first 8
+    //     each followed by two reads of stage t + 1's set 0 and the first 7 by
+    //     one DMA of stage t + 3's first half into slot t % 3.
+    // Every memory instruction sits between two SMFMACs (sched_barrier), so
+    // the matrix core keeps issuing while they are queued, and the last reads
+    // of a set are issued four SMFMACs before the set is first used.  Stages
+    // past the last one load stage nk - 1 again into their (free) slot instead
+    // of branching; those copies are never read and have landed before LDS is
+    // reused.
+    constexpr int kHalf = C::DMA_PER_STAGE / 2;
+    static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8, "DMA split");
     const int nk = K / 64;  // even: K is a multiple of 128
+    // instruction i of half `half` of stage u, into the ring slot at byte offset soff
+    auto dma_half = [&](int u, int soff, int half, int i) {
+        dma_k(min(u, nk - 1), uint32_t(soff), half * kHalf + i);
+    };
     __builtin_amdgcn_s_waitcnt(0);
     for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, 0, k);
-    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, C::STAGE, k);
-    wait_vmcnt<C::DMA_PER_STAGE>();
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(min(1, nk - 1), C::STAGE, k);
+    for (int i = 0; i < kHalf; ++i) dma_half(2, 2 * C::STAGE, 0, i);
+    wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
     block_barrier();
-    Frags f0, f1;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) lds_k(0, 0, f0, k);
-    // The last two stages load stage nk - 1 once more into the free slot
-    // instead of branching around the loads: every stage body is the same
-    // straight-line code.  The copies are never read and have landed before
-    // LDS is reused.
+    for (int n = 0; n < 16; ++n) read_n(0, 0, fr[0], n);
+
+    // byte offsets of slots t % 3, (t + 1) % 3, (t + 2) % 3, rotated per stage
+    int cur = 0, nxt = C::STAGE, aft = 2 * C::STAGE;
     for (int t = 0; t < nk; ++t) {
-        const int slot = t % 3;
-        const int tl = min(t + 2, nk - 1);
-        const uint32_t lslot = uint32_t(((t + 2) % 3) * C::STAGE);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-            mma_k(f0, k);
-            if (k < C::DMA_PER_STAGE) dma_k(tl, lslot, k);
-            lds_k(slot, 1, f1, k);
+            mma(fr[0], k);
+            if (k < 8) {
+                read_n(cur, 1, fr[1], 2 * k);
+                read_n(cur, 1, fr[1], 2 * k + 1);
+            } else if (k - 8 < kHalf) {
+                dma_half(t + 2, aft, 1, k - 8);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            mma_k(f1, k);
+        for (int k = 0; k < 4; ++k) {
+            mma(fr[1], k);
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();  // stage t + 1 has landed
         block_barrier();
-        const int nslot = (t + 1) % 3;  // stale after the last stage, never used
 #pragma unroll
-        for (int k = 8; k < 16; ++k) {
-            mma_k(f1, k);
-            lds_k(nslot, 0, f0, 2 * (k - 8));
-            lds_k(nslot, 0, f0, 2 * (k - 8) + 1);
+        for (int k = 4; k < 16; ++k) {
+            mma(fr[1], k);
+            if (k < 12) {
+                read_n(nxt, 0, fr[0], 2 * (k - 4));
+                read_n(nxt, 0, fr[0], 2 * (k - 4) + 1);
+            }
+            if (k - 4 < kHalf) dma_half(t + 3, cur, 0, k - 4);
             __builtin_amdgcn_sched_barrier(0);
         }
+        const int freed = cur;
+        cur = nxt;
+        nxt = aft;
+        aft = freed;
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // all waves done with the ring before LDS is reused
