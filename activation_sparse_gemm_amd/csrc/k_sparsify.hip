@@ -94,9 +94,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ LB, int M, int K,
     uint16_t* __restrict__ values, uint8_t* __restrict__ meta, float* __restrict__ scale,
     uint16_t* __restrict__ T) {
+    constexpr int R = RT * 16;
     __shared__ double red_norm[kMaxWaves][kRows][2];
     __shared__ int exact_row[kRows];
-    __shared__ float red_T[RT > 0 ? kMaxWaves : 1][kRows][RT > 0 ? RT * 16 : 1];
+    // per-wave LB chunk (R rows x 256 B, XOR-swizzled 16-byte pieces); after
+    // the main loop the same memory holds the cross-wave T partials
+    constexpr int kLbBytes = RT > 0 ? R * 256 : 64;
+    __shared__ __attribute__((aligned(16))) char lbw[kMaxWaves][kLbBytes];
+    static_assert(sizeof(lbw) >= sizeof(float) * kMaxWaves * kRows * (RT > 0 ? R : 1),
+                  "T partials fit in the LB staging area");
+    float(*red_T)[kRows][RT > 0 ? R : 1] =
+        reinterpret_cast<float(*)[kRows][RT > 0 ? R : 1]>(&lbw[0][0]);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -126,12 +134,15 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4*>(xrow + k + 8 * i);
 
-        u32x4 lbv[RT > 0 ? RT : 1][4];
+        // LB rows x this chunk's 128 channels, read as whole row segments
+        // (instruction j: rows 4j .. 4j+3, lane l -> row 4j + l / 16, 16-byte
+        // piece l % 16) and put in the wave's LDS area for the MFMA B operand
+        u32x4 lbraw[RT > 0 ? R / 4 : 1];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            const uint16_t* lbrow = LB + size_t(16 * t + r) * size_t(K) + k;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) lbv[t][i] = *reinterpret_cast<const u32x4*>(lbrow + 8 * i);
+        for (int j = 0; j < (RT > 0 ? R / 4 : 0); ++j) {
+            const int lr = 4 * j + (lane >> 4);
+            lbraw[j] = *reinterpret_cast<const u32x4*>(LB + size_t(lr) * size_t(K) +
+                                                       size_t(c) * kChunk + 8 * (lane & 15));
         }
 
         // dense row norm
@@ -174,15 +185,33 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
             }
         }
 
-        // T += X LB^T over these channels
+        // T += X LB^T over these channels; B operand of step i: LB row
+        // 16 t + r, channels 32 q + 8 i .. +8 of the chunk
+        if constexpr (RT > 0) {
+            char* lb = lbw[wave];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    __builtin_bit_cast(bf16x8, xv[i]), __builtin_bit_cast(bf16x8, lbv[t][i]),
-                    acc[t], 0, 0, 0);
+            for (int j = 0; j < R / 4; ++j) {
+                const int lr = 4 * j + (lane >> 4);
+                *reinterpret_cast<u32x4*>(lb + lr * 256 + 16 * ((lane & 15) ^ (lr & 15))) =
+                    lbraw[j];
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bf16x8 bv = *reinterpret_cast<const bf16x8*>(
+                        lb + (16 * t + r) * 256 + 16 * ((4 * q + i) ^ r));
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, xv[i]), bv, acc[t], 0, 0, 0);
+                }
+            }
+            // the next chunk's writes must not overtake this chunk's reads
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
     }
 
@@ -195,6 +224,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         red_norm[wave][r][0] = n2;
         red_norm[wave][r][1] = nt2;
     }
+    __syncthreads();  // every wave is done with its LB area before it holds T partials
     // accumulator layout of a 16x16 tile: lane (n = l % 16, q) holds rows 4q..4q+3
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
@@ -235,7 +265,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         if (lane == 0) scale[m0 + rr] = b > 0.0 ? float(sqrt(a / b)) : 1.0f;
     }
     if constexpr (RT > 0) {
-        constexpr int R = RT * 16;
         for (int idx = threadIdx.x; idx < kRows * R; idx += blockDim.x) {
             const int rr = idx / R, cc = idx % R;
             float s = 0.f;
