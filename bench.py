@@ -3,16 +3,19 @@
     python bench.py [--steps K] [--warmup W] [--workload mlp_up] [--no-cpu]
 
 A step is one call of lynx_linear_sparse_lora (sparsify + 2:4 sparse-MFMA GEMM
-with the LoRA epilogue) on one batch of synthetic input already resident in
-HBM.  The default workload is the DiT MLP up-projection, X [4096 x 3072] ->
-Y [4096 x 12288], rank-64 LoRA.  Inputs rotate over three independent sets
+with the LoRA epilogue) per layer of the workload on one batch of synthetic
+input already resident in HBM.  The default workload is the DiT MLP
+up-projection, X [4096 x 3072] -> Y [4096 x 12288], rank-64 LoRA; `block` is
+the CFG-batched DiT block's four linears (M = 9216: QKV, attention-out, MLP-up,
+MLP-down) in sequence.  Inputs rotate over three independent sets
 (X, W, LA, LB, Y, workspace) so the working set (> 600 MB) exceeds the 256 MB
 last-level cache.
 
-Also timed with the same protocol: the dense bf16 MFMA layer (lynx_linear_dense,
-the speedup baseline), the sparsifier alone and the GEMM alone (split of the
-sparse layer's time), and torch.matmul (hipBLASLt) as a sanity reference that
-the library never calls.  The CPU oracle is timed on a bounded sample on the
+Then the sparse layer, the dense bf16 MFMA layer (lynx_linear_dense, the
+speedup baseline), the sparsifier alone and the GEMM alone (split of the sparse
+layer's time) and torch.matmul (hipBLASLt, a reference the library never calls)
+take turns in rounds of --calls calls; each reports the median over --rounds
+rounds, so all of them are timed under the same clock and power state.  The CPU oracle is timed on a bounded sample on the
 host (cpu_baseline).  Prints ONE JSON line.
 """
 from __future__ import annotations
@@ -30,6 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_DENSE_BF16_TFLOPS = 2516.6    # MI355X dense bf16 MFMA, AMD published
 PEAK_SPARSE_BF16_TFLOPS = 5033.2   # 2:4 structured-sparse bf16 (dense-equivalent), AMD published
 PEAK_HBM_GBS = 8000.0
+METRIC = "dense-equiv TFLOP/s + % sparse-MFMA peak; speedup vs dense bf16 GEMM, M4096 K3072"
 
 
 def parse():
@@ -37,9 +41,14 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="mlp_up", choices=["tiny", "qkv", "mlp_up", "mlp_down"])
+    p.add_argument("--workload", default="mlp_up",
+                   choices=["tiny", "qkv", "mlp_up", "mlp_down", "block"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--sets", type=int, default=3)
+    p.add_argument("--rounds", type=int, default=7,
+                   help="rounds of the interleaved comparison timing")
+    p.add_argument("--calls", type=int, default=20,
+                   help="calls per function and round in the comparison timing")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run a plain 256 MiB streaming kernel (torch.neg) three "
                         "times, the reference for HBM byte counters")
@@ -63,6 +72,28 @@ def time_region(fn, steps, warmup, stream):
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def time_interleaved(fns: dict, rounds: int, calls: int, stream) -> dict:
+    """Median over `rounds` of the average ms per call of each fn, the fns
+    taking turns (`calls` calls each per round) so that all of them run under
+    the same clock and power state; HIP events on `stream`."""
+    import statistics
+
+    import torch
+    per = {name: [] for name in fns}
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    for _ in range(rounds):
+        for name, fn in fns.items():
+            torch.cuda.synchronize()
+            start.record(stream)
+            for i in range(calls):
+                fn(i)
+            end.record(stream)
+            torch.cuda.synchronize()
+            per[name].append(start.elapsed_time(end) / calls)
+    return {name: statistics.median(v) for name, v in per.items()}
 
 
 def cpu_baseline(L, min_s=10.0, max_rows_growth=8.0):
@@ -193,59 +224,73 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
-    base = make_config(args.workload)[0]
-    M, K, N, R = base.M, base.K, base.N, base.R
+    layers = make_config(args.workload)   # one layer, or the block's four in sequence
 
     def to_dev(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    # sets[s][j]: device tensors of layer j in input set s (set 0 = the seeded
+    # workload itself, the others independent draws of the same shapes)
     sets = []
     for s in range(args.sets):
-        L = base if s == 0 else make_layer(M, K, N, base.kind, seed=100 + s, R=R, name=base.name)
-        X, W, LA, LB = to_dev(L.X), to_dev(L.W), to_dev(L.LA), to_dev(L.LB)
-        ws = torch.empty(lynx.workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        packed = lynx.sparsify(X, LB)
-        sets.append(dict(X=X, W=W, LA=LA, LB=LB, ws=ws, Y=Y, Yd=Yd, packed=packed))
+        row = []
+        for j, base in enumerate(layers):
+            L = base if s == 0 else make_layer(base.M, base.K, base.N, base.kind,
+                                               seed=100 + 10 * s + j, R=base.R, name=base.name)
+            X, W, LA, LB = to_dev(L.X), to_dev(L.W), to_dev(L.LA), to_dev(L.LB)
+            M, K, N, R = L.M, L.K, L.N, L.R
+            ws = torch.empty(lynx.workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            packed = lynx.sparsify(X, LB)
+            row.append(dict(X=X, W=W, LA=LA, LB=LB, ws=ws, Y=Y, Yd=Yd, packed=packed))
+        sets.append(row)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     S = len(sets)
 
     def step(i):
-        d = sets[i % S]
-        lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"], Y=d["Y"], workspace=d["ws"])
+        for d in sets[i % S]:
+            lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"], Y=d["Y"],
+                                    workspace=d["ws"])
 
     def dense(i):
-        d = sets[i % S]
-        lynx.linear_dense(d["X"], d["W"], Y=d["Yd"])
+        for d in sets[i % S]:
+            lynx.linear_dense(d["X"], d["W"], Y=d["Yd"])
 
     def gemm_only(i):
-        d = sets[i % S]
-        v, m, sc, T = d["packed"]
-        lynx.linear_sparse_lora_packed(v, m, sc, T, d["W"], d["LA"], Y=d["Y"])
+        for d in sets[i % S]:
+            v, m, sc, T = d["packed"]
+            lynx.linear_sparse_lora_packed(v, m, sc, T, d["W"], d["LA"], Y=d["Y"])
 
     def sparsify_only(i):
-        d = sets[i % S]
-        v, m, sc, T = d["packed"]
-        lynx.sparsify(d["X"], d["LB"], out=dict(values=v, meta=m, scale=sc, T=T))
+        for d in sets[i % S]:
+            v, m, sc, T = d["packed"]
+            lynx.sparsify(d["X"], d["LB"], out=dict(values=v, meta=m, scale=sc, T=T))
 
     def torch_mm(i):
-        d = sets[i % S]
-        torch.matmul(d["X"], d["W"].t(), out=d["Yd"])
+        for d in sets[i % S]:
+            torch.matmul(d["X"], d["W"].t(), out=d["Yd"])
 
     torch.cuda.synchronize()
+    # the headline: K consecutive steps after W warm-up steps
     ms = time_region(step, args.steps, args.warmup, stream)
-    ms_dense = time_region(dense, args.steps, args.warmup, stream)
-    ms_gemm = time_region(gemm_only, args.steps, args.warmup, stream)
-    ms_k1 = time_region(sparsify_only, args.steps, args.warmup, stream)
-    ms_torch = time_region(torch_mm, args.steps, args.warmup, stream)
+    # comparisons: the sparse layer, the dense layer, the split of the sparse
+    # layer and hipBLASLt take turns, so each sees the same clock and power
+    # state (a sustained matrix-core load lowers the clock within milliseconds)
+    med = time_interleaved({"sparse": step, "dense": dense, "gemm": gemm_only,
+                            "sparsify": sparsify_only, "torch": torch_mm},
+                           rounds=args.rounds, calls=args.calls, stream=stream)
+    ms_sparse_i, ms_dense = med["sparse"], med["dense"]
+    ms_gemm, ms_k1, ms_torch = med["gemm"], med["sparsify"], med["torch"]
 
-    flops = 2 * M * N * K + 2 * M * R * (K + N)           # dense-equivalent, whole layer
+    # dense-equivalent flops of a step (all layers)
+    flops = sum(2 * L.M * L.N * L.K + 2 * L.M * L.R * (L.K + L.N) for L in layers)
+    dense_flops = sum(2 * L.M * L.N * L.K for L in layers)
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: the 2:4 GEMM; algorithmic flops = products on kept values
     # (M N K/2 multiply-adds) + LoRA up-projection (M R N multiply-adds)
-    k2_alg_flops = M * N * K + 2 * M * R * N
+    k2_alg_flops = sum(L.M * L.N * L.K + 2 * L.M * L.R * L.N for L in layers)
     k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
     traffic = traffic_for(K2_SRC, args.workload)
     if args.copy_calibration:
@@ -255,11 +300,19 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    cpu = None if args.no_cpu else cpu_baseline(base)
+    cpu = None if args.no_cpu else cpu_baseline(layers[-1] if len(layers) == 1 else layers[2])
 
+    shapes = [f"{L.name}: X[{L.M}x{L.K}] -> Y[{L.M}x{L.N}]" for L in layers]
+    kinds = sorted({L.kind for L in layers})
+    first = layers[0]
+    config = {"workload": f"{args.workload}: " + "; ".join(shapes) +
+                          f"; bf16, rank-{first.R} LoRA, {'/'.join(kinds)} activations, "
+                          f"{S} rotating input sets",
+              "layers": [{"M": L.M, "K": L.K, "N": L.N, "R": L.R} for L in layers]}
+    if len(layers) == 1:
+        config.update({"M": first.M, "K": first.K, "N": first.N, "R": first.R})
     rec = {
-        "metric": "dense-equiv TFLOP/s of the sparse+LoRA linear (also % of bf16 sparse-MFMA "
-                  "peak and speedup vs the in-library dense bf16 GEMM), M4096 K3072",
+        "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -271,16 +324,15 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{base.name}: X[{M}x{K}] bf16 -> Y[{M}x{N}], rank-{R} LoRA, "
-                               f"heavy-tailed activations, {S} rotating input sets",
-                   "M": M, "K": K, "N": N, "R": R},
+        "config": config,
         "pct_sparse_peak": round(100 * tflops / PEAK_SPARSE_BF16_TFLOPS, 2),
         "pct_dense_peak": round(100 * tflops / PEAK_DENSE_BF16_TFLOPS, 2),
-        "speedup_vs_dense": round(ms_dense / ms, 3),
-        "dense_tflops": round(2 * M * N * K / (ms_dense * 1e-3) / 1e12, 2),
-        "dense_ms": round(ms_dense, 5),
+        "speedup_vs_dense": round(ms_dense / ms_sparse_i, 3),
+        "speedup_vs_torch_matmul": round(ms_torch / ms_sparse_i, 3),
+        "interleaved_ms": {"sparse_layer": round(ms_sparse_i, 5), "dense_layer": round(ms_dense, 5),
+                           "torch_matmul": round(ms_torch, 5)},
+        "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2),
         "split_ms": {"sparsify": round(ms_k1, 5), "sparse_gemm_lora": round(ms_gemm, 5)},
-        "torch_matmul_ms": round(ms_torch, 5),
         "roofline": {"bound": "mfma", "kernel": "gemm_sparse32 (2:4 SMFMAC + LoRA up-projection)",
                      "achieved": round(k2_tflops, 2), "peak": PEAK_DENSE_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k2_tflops / PEAK_DENSE_BF16_TFLOPS, 4),
