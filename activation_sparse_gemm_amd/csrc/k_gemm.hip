@@ -33,6 +33,8 @@
 // remapped to give each XCD a contiguous range of tiles, and tiles are
 // rasterized in groups of 8 tile-rows so the ~32 workgroups resident on one
 // XCD share A rows and W rows in that XCD's L2.
+#include <type_traits>
+
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -434,29 +436,61 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     //     one DMA of stage t + 3's first half into slot t % 3.
     // Every memory instruction sits between two SMFMACs (sched_barrier), so
     // the matrix core keeps issuing while they are queued, and the last reads
-    // of a set are issued four SMFMACs before the set is first used.  Stages
-    // past the last one load stage nk - 1 again into their (free) slot instead
-    // of branching; those copies are never read and have landed before LDS is
-    // reused.
+    // of a set are issued four SMFMACs before the set is first used.
+    // The two stages after the last one carry the LoRA operands through the
+    // same slots: "stage" nk is the tile's 256 rows of T (slot nk % 3) and
+    // "stage" nk + 1 its 256 rows of LA (slot (nk + 1) % 3), 8 DMA
+    // instructions each (128-byte rows, ranks past R and rows past M or N read
+    // as zeros), so they arrive while the last stages compute.  Slot
+    // (nk + 2) % 3 is left for the epilogue.
     constexpr int kHalf = C::DMA_PER_STAGE / 2;
     static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8, "DMA split");
+    constexpr int kLoraHalf = 4;  // DMA instructions per half of a LoRA stage
     const int nk = K / 64;  // even: K is a multiple of 128
-    // instruction i of half `half` of stage u, into the ring slot at byte offset soff
-    auto dma_half = [&](int u, int soff, int half, int i) {
-        dma_k(min(u, nk - 1), uint32_t(soff), half * kHalf + i);
+    enum { kMain, kT, kLA, kNone };
+    const i32x4 rsT = make_rsrc(T, uint32_t(M) * uint32_t(2 * R));
+    const i32x4 rsL = make_rsrc(LA, uint32_t(N) * uint32_t(2 * R));
+    // LoRA DMA instruction j (0..7) of wave w: LDS rows 8 (w + 4j) + l/8 of
+    // the slot (128 B each), 16-byte chunk l % 8 in swizzled position
+    auto dma_lora = [&](bool is_T, int soff, int j) {
+        const int row = 8 * (wave + 4 * j) + (lane >> 3);
+        const int c = (lane & 7) ^ swz128(row);
+        const int base = is_T ? m0 : n0;
+        const int voff = 8 * c < R ? (base + row) * 2 * R + 16 * c : 0x7FFFFFF0;
+        dma16(lds0 + uint32_t(soff) + 1024 * (wave + 4 * j), voff, is_T ? rsT : rsL, 0);
     };
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, 0, k);
-    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(min(1, nk - 1), C::STAGE, k);
-    for (int i = 0; i < kHalf; ++i) dma_half(2, 2 * C::STAGE, 0, i);
-    wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
-    block_barrier();
-#pragma unroll
-    for (int n = 0; n < 16; ++n) read_n(0, 0, fr[0], n);
+    // instruction i (0..kHalf-1) of half `half` of a stage of kind KIND
+    auto dma_grp = [&](auto kind_c, int u, int soff, int half, int i) {
+        constexpr int KIND = decltype(kind_c)::value;
+        if constexpr (KIND == kMain) {
+            dma_k(u, uint32_t(soff), half * kHalf + i);
+        } else if constexpr (KIND == kT || KIND == kLA) {
+            if (i < kLoraHalf && R > 0) dma_lora(KIND == kT, soff, half * kLoraHalf + i);
+        }
+    };
+    // s_waitcnt for "stage t + 1 has landed" when stage t + 2 is of kind NEXT2
+    auto wait_next = [&](auto next2_c) {
+        constexpr int NEXT2 = decltype(next2_c)::value;
+        if constexpr (NEXT2 == kMain) {
+            wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();
+        } else {
+            if (R > 0) {
+                wait_vmcnt_lgkm0<2 * kLoraHalf>();
+            } else {
+                wait_vmcnt_lgkm0<0>();
+            }
+        }
+    };
+    using IMain = std::integral_constant<int, kMain>;
+    using IT = std::integral_constant<int, kT>;
+    using ILA = std::integral_constant<int, kLA>;
+    using INone = std::integral_constant<int, kNone>;
 
     // byte offsets of slots t % 3, (t + 1) % 3, (t + 2) % 3, rotated per stage
     int cur = 0, nxt = C::STAGE, aft = 2 * C::STAGE;
-    for (int t = 0; t < nk; ++t) {
+    // one stage: G2 = kind of stage t + 2 (second half issued here), G3 = kind
+    // of stage t + 3 (first half issued here)
+    auto stage = [&](int t, auto g2, auto g3) {
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             mma(fr[0], k);
@@ -464,7 +498,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 read_n(cur, 1, fr[1], 2 * k);
                 read_n(cur, 1, fr[1], 2 * k + 1);
             } else if (k - 8 < kHalf) {
-                dma_half(t + 2, aft, 1, k - 8);
+                dma_grp(g2, t + 2, aft, 1, k - 8);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -473,7 +507,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             mma(fr[1], k);
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();  // stage t + 1 has landed
+        wait_next(g2);  // stage t + 1 has landed
         block_barrier();
 #pragma unroll
         for (int k = 4; k < 16; ++k) {
@@ -482,53 +516,57 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 read_n(nxt, 0, fr[0], 2 * (k - 4));
                 read_n(nxt, 0, fr[0], 2 * (k - 4) + 1);
             }
-            if (k - 4 < kHalf) dma_half(t + 3, cur, 0, k - 4);
+            if (k - 4 < kHalf) dma_grp(g3, t + 3, cur, 0, k - 4);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int freed = cur;
         cur = nxt;
         nxt = aft;
         aft = freed;
-    }
+    };
+
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // all waves done with the ring before LDS is reused
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, 0, k);
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, C::STAGE, k);
+    if (nk > 2) {
+        for (int i = 0; i < kHalf; ++i) dma_grp(IMain{}, 2, 2 * C::STAGE, 0, i);
+        wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
+    } else {
+        for (int i = 0; i < kHalf; ++i) dma_grp(IT{}, 2, 2 * C::STAGE, 0, i);
+        if (R > 0) {
+            wait_vmcnt<C::DMA_PER_STAGE + kLoraHalf>();
+        } else {
+            wait_vmcnt<C::DMA_PER_STAGE>();
+        }
+    }
+    block_barrier();
+#pragma unroll
+    for (int n = 0; n < 16; ++n) read_n(0, 0, fr[0], n);
+
+    for (int t = 0; t < nk - 3; ++t) stage(t, IMain{}, IMain{});
+    if (nk >= 3) stage(nk - 3, IMain{}, IT{});
+    stage(nk - 2, IT{}, ILA{});
+    stage(nk - 1, ILA{}, INone{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // LoRA operands landed; all waves done with the ring
 
     const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
     // ---- LoRA up-projection: acc += (T / s) LA^T ----------------------------
     if (R > 0) {
-        char* Ts = smem;
-        char* Ls = smem + 32 * 1024;
-        u32x4 traw[8], lraw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = tid + NT * j;
-            const int row = c >> 3, kc = min(8 * (c & 7), R - 8);
-            traw[j] = *reinterpret_cast<const u32x4*>(T + size_t(min(m0 + row, M - 1)) * R + kc);
-            lraw[j] = *reinterpret_cast<const u32x4*>(LA + size_t(min(n0 + row, N - 1)) * R + kc);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = tid + NT * j;
-            const int row = c >> 3, ch = c & 7;
-            const int off = row * 128 + 16 * (ch ^ swz128(row));
-            const bool live = 8 * ch < R;
-            const float inv = 1.0f / s_lds[row];
-            const u32x4 raw = traw[j];
-            u32x4 tv;
-            tv.x = pack_bf16x2(bf16_lo(raw.x) * inv, bf16_hi(raw.x) * inv);
-            tv.y = pack_bf16x2(bf16_lo(raw.y) * inv, bf16_hi(raw.y) * inv);
-            tv.z = pack_bf16x2(bf16_lo(raw.z) * inv, bf16_hi(raw.z) * inv);
-            tv.w = pack_bf16x2(bf16_lo(raw.w) * inv, bf16_hi(raw.w) * inv);
-            const u32x4 zero = {0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(Ts + off) = live ? tv : zero;
-            *reinterpret_cast<u32x4*>(Ls + off) = live ? lraw[j] : zero;
-        }
-        __syncthreads();
+        const char* Ts = smem + (nk % 3) * C::STAGE;
+        const char* Ls = smem + ((nk + 1) % 3) * C::STAGE;
         // T / s is dense; it is fed to the same SMFMAC as two exactly-2:4 halves
         // with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per group):
         // over channels [16h, 16h+16) of a 32-rank step the even dwords of the
         // row are positions 0,1 of each group and the odd dwords positions 2,3.
-        // LA supplies the B operand exactly as W does in the main loop.
+        // T / s is rounded to bf16 here.  LA supplies the B operand exactly as
+        // W does in the main loop.
+        float inv[4];
+#pragma unroll
+        for (int a = 0; a < 4; ++a) inv[a] = 1.0f / s_lds[wm * 128 + 32 * a + r];
+        auto scaled = [](uint32_t w, float f) {
+            return pack_bf16x2(bf16_lo(w) * f, bf16_hi(w) * f);
+        };
         for (int ks = 0; ks < (R + 31) / 32; ++ks) {
             const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
             const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128), ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
@@ -546,8 +584,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 const int row = (wm * 128 + 32 * a + r) * 128;
                 const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
                 const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
-                const bf16x8 te = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.z, t1.x, t1.z});
-                const bf16x8 to = __builtin_bit_cast(bf16x8, u32x4{t0.y, t0.w, t1.y, t1.w});
+                const float f = inv[a];
+                const bf16x8 te = __builtin_bit_cast(
+                    bf16x8, u32x4{scaled(t0.x, f), scaled(t0.z, f), scaled(t1.x, f), scaled(t1.z, f)});
+                const bf16x8 to = __builtin_bit_cast(
+                    bf16x8, u32x4{scaled(t0.y, f), scaled(t0.w, f), scaled(t1.y, f), scaled(t1.w, f)});
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(te, bl[b], acc[a][b],
@@ -562,7 +603,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     // ---- epilogue: y = s * acc, bf16, 16 rows at a time through LDS ---------
     // rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4; the
     // half p = 0 / 1 (e < 8 / e >= 8) covers rows 0..15 / 16..31.
-    char* ep = smem + C::EPI_OFF + wave * 4096;  // 16 rows x 128 cols bf16
+    // scratch in the slot the LoRA operands left free
+    char* ep = smem + ((nk + 2) % 3) * C::STAGE + wave * 4096;  // 16 rows x 128 cols bf16
     const bool vec_ok = (N & 7) == 0;
 #pragma unroll
     for (int a = 0; a < 4; ++a) {

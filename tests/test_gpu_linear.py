@@ -34,7 +34,7 @@ SHAPES = [
     (1, 128, 1, 16), (17, 256, 40, 32), (100, 640, 130, 48), (300, 1152, 257, 64),
     (64, 128, 64, 0), (513, 384, 520, 64), (37, 2048, 300, 16),
     (1000, 640, 1100, 64), (777, 1152, 1030, 48), (520, 256, 1288, 16), (1024, 512, 1024, 0),
-    (1280, 3072, 768, 32),
+    (1280, 3072, 768, 32), (1024, 128, 1024, 64), (1024, 384, 1100, 32),
 ]
 
 
