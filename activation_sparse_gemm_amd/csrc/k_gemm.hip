@@ -312,7 +312,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ LA,
     uint16_t* __restrict__ Y, int M, int N, int K, int R) {
     using C = Cfg<true>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+    // ring of 3 stages, the tile's s, and the epilogue's staging rows
+    constexpr int kEpiOff = C::SCALE_OFF + BM * 4;
+    constexpr int kEpiWave = 8 * 256;  // 8 rows x 128 columns bf16 per wave
+    constexpr int kLds = kEpiOff + 4 * kEpiWave;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -321,9 +326,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const int wm = wave & 1, wn = wave >> 1;
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int ntiles = tiles_m * tiles_n;
 
     // ---- DMA addressing ----------------------------------------------------
     // values: instruction j of wave w moves the 1 KB value tile of row block
@@ -340,22 +343,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const i32x4 rsA = make_rsrc(values, uint32_t(Mp) * uint32_t(K));
     const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
     const i32x4 rsM = make_rsrc(meta, uint32_t(Mp) * uint32_t(K / 8));
+    const i32x4 rsT = make_rsrc(T, uint32_t(M) * uint32_t(2 * R));
+    const i32x4 rsL = make_rsrc(LA, uint32_t(N) * uint32_t(2 * R));
+    const i32x4 rsS = make_rsrc(scale, uint32_t(M) * 4u);
     int voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA];
+    auto set_tile_offsets = [&](int tm0, int tn0) {
 #pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j) {
-        const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
-        voffA[j] = (m0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
-    }
+        for (int j = 0; j < C::A_DMA; ++j) {
+            const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
+            voffA[j] = (tm0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
+        }
 #pragma unroll
-    for (int j = 0; j < C::B_DMA; ++j) {
-        const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
-        voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz128(row));
-    }
+        for (int j = 0; j < C::B_DMA; ++j) {
+            const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
+            voffB[j] = (tn0 + row) * 2 * K + 16 * (ph ^ swz128(row));
+        }
 #pragma unroll
-    for (int j = 0; j < C::M_DMA; ++j) {
-        const int blk = 2 * (wave + 4 * j) + (lane >> 5);
-        voffM[j] = (m0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
-    }
+        for (int j = 0; j < C::M_DMA; ++j) {
+            const int blk = 2 * (wave + 4 * j) + (lane >> 5);
+            voffM[j] = (tm0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
+        }
+    };
     // one of the 14 DMA instructions of a stage (4 value tiles, 2 meta, 8 W)
     auto dma_k = [&](int t, uint32_t slot_off, int k) {
         const uint32_t base = lds0 + slot_off;
@@ -409,10 +417,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     };
 
     f32x16 acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
     auto mma = [&](const Frags& f, int k) {
         const int a = k & 3, b = k >> 2;
         const bf16x16 bv = __builtin_shufflevector(f.blo[b], f.bhi[b], 0, 1, 2, 3, 4, 5, 6, 7, 8,
@@ -420,13 +424,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.v[a], bv, acc[a][b], f.i[a], 0, 0);
     };
 
-    // s of the tile's 256 rows into LDS (rows past M repeat the last row)
-    reinterpret_cast<float*>(smem + C::SCALE_OFF)[tid] = scale[min(m0 + tid, M - 1)];
-
     // Ring schedule.  Stage u's 14 DMA instructions go out in two halves: the
     // first 7 in stage u - 3's sub-step 1, right after the barrier that frees
     // slot u % 3, and the other 7 in stage u - 2's sub-step 0.  Per stage t
-    // (slot t % 3; set 0 holds sub-step 0's fragments):
+    // (set 0 holds sub-step 0's fragments):
     //   sub-step 0: 16 SMFMACs on set 0; two reads of set 1 (same slot) after
     //     each of the first 8, one DMA of stage t + 2's second half after each
     //     of the next 7;
@@ -437,19 +438,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     // Every memory instruction sits between two SMFMACs (sched_barrier), so
     // the matrix core keeps issuing while they are queued, and the last reads
     // of a set are issued four SMFMACs before the set is first used.
-    // The two stages after the last one carry the LoRA operands through the
-    // same slots: "stage" nk is the tile's 256 rows of T (slot nk % 3) and
-    // "stage" nk + 1 its 256 rows of LA (slot (nk + 1) % 3), 8 DMA
-    // instructions each (128-byte rows, ranks past R and rows past M or N read
-    // as zeros), so they arrive while the last stages compute.  Slot
-    // (nk + 2) % 3 is left for the epilogue.
+    // The two stages after a tile's last one carry its LoRA operands through
+    // the same slots: "stage" nk is the tile's 256 rows of T and "stage"
+    // nk + 1 its 256 rows of LA, 8 DMA instructions each (128-byte rows; ranks
+    // past R and rows past M or N read as zeros), so they arrive while the
+    // last stages compute; stage nk also brings the tile's 256 values of s
+    // (rows past M read as 0) into their own LDS table.  Every load of the
+    // kernel is one of these DMA instructions, so all vmcnt waits are explicit
+    // and count them exactly; loads complete in order, so a wait that leaves
+    // the n loads issued after a stage in flight has that stage landed,
+    // whatever the epilogue's stores in between are doing.  "Stage" nk + 2 is the next tile's stage 0: the
+    // workgroup is persistent (tiles blockIdx.x, + gridDim.x, ...), and the
+    // next tile's first loads are in flight during this tile's LoRA and
+    // epilogue.
     constexpr int kHalf = C::DMA_PER_STAGE / 2;
     static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8, "DMA split");
-    constexpr int kLoraHalf = 4;  // DMA instructions per half of a LoRA stage
+    constexpr int kLoraHalf = 4;  // T or LA DMA instructions per half of a LoRA stage
     const int nk = K / 64;  // even: K is a multiple of 128
-    enum { kMain, kT, kLA, kNone };
-    const i32x4 rsT = make_rsrc(T, uint32_t(M) * uint32_t(2 * R));
-    const i32x4 rsL = make_rsrc(LA, uint32_t(N) * uint32_t(2 * R));
+    enum { kMain, kT, kLA, kNext0 };
+    int m0 = 0, n0 = 0;
     // LoRA DMA instruction j (0..7) of wave w: LDS rows 8 (w + 4j) + l/8 of
     // the slot (128 B each), 16-byte chunk l % 8 in swizzled position
     auto dma_lora = [&](bool is_T, int soff, int j) {
@@ -459,13 +466,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         const int voff = 8 * c < R ? (base + row) * 2 * R + 16 * c : 0x7FFFFFF0;
         dma16(lds0 + uint32_t(soff) + 1024 * (wave + 4 * j), voff, is_T ? rsT : rsL, 0);
     };
-    // instruction i (0..kHalf-1) of half `half` of a stage of kind KIND
+    // wave w's quarter of the tile's s: rows 64 w + l
+    auto dma_scale = [&]() {
+        dma4(lds0 + C::SCALE_OFF + 256 * wave, (m0 + 64 * wave + lane) * 4, rsS, 0);
+    };
+    bool has_next = false;
+    // instruction i (0..kHalf-1) of half `half` of a stage of kind KIND; the
+    // T stage's first half also carries the s table
     auto dma_grp = [&](auto kind_c, int u, int soff, int half, int i) {
         constexpr int KIND = decltype(kind_c)::value;
         if constexpr (KIND == kMain) {
             dma_k(u, uint32_t(soff), half * kHalf + i);
         } else if constexpr (KIND == kT || KIND == kLA) {
             if (i < kLoraHalf && R > 0) dma_lora(KIND == kT, soff, half * kLoraHalf + i);
+            if (KIND == kT && half == 0 && i == kLoraHalf) dma_scale();
+        } else {
+            if (has_next) dma_k(0, uint32_t(soff), half * kHalf + i);
         }
     };
     // s_waitcnt for "stage t + 1 has landed" when stage t + 2 is of kind NEXT2
@@ -473,6 +489,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         constexpr int NEXT2 = decltype(next2_c)::value;
         if constexpr (NEXT2 == kMain) {
             wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();
+        } else if constexpr (NEXT2 == kT) {
+            if (R > 0) {
+                wait_vmcnt_lgkm0<2 * kLoraHalf + 1>();
+            } else {
+                wait_vmcnt_lgkm0<1>();
+            }
         } else {
             if (R > 0) {
                 wait_vmcnt_lgkm0<2 * kLoraHalf>();
@@ -484,7 +506,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     using IMain = std::integral_constant<int, kMain>;
     using IT = std::integral_constant<int, kT>;
     using ILA = std::integral_constant<int, kLA>;
-    using INone = std::integral_constant<int, kNone>;
+    using INext0 = std::integral_constant<int, kNext0>;
 
     // byte offsets of slots t % 3, (t + 1) % 3, (t + 2) % 3, rotated per stage
     int cur = 0, nxt = C::STAGE, aft = 2 * C::STAGE;
@@ -525,129 +547,177 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         aft = freed;
     };
 
-    __builtin_amdgcn_s_waitcnt(0);
-    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, 0, k);
-    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, C::STAGE, k);
-    if (nk > 2) {
-        for (int i = 0; i < kHalf; ++i) dma_grp(IMain{}, 2, 2 * C::STAGE, 0, i);
-        wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
-    } else {
-        for (int i = 0; i < kHalf; ++i) dma_grp(IT{}, 2, 2 * C::STAGE, 0, i);
-        if (R > 0) {
-            wait_vmcnt<C::DMA_PER_STAGE + kLoraHalf>();
-        } else {
-            wait_vmcnt<C::DMA_PER_STAGE>();
-        }
-    }
-    block_barrier();
-#pragma unroll
-    for (int n = 0; n < 16; ++n) read_n(0, 0, fr[0], n);
-
-    for (int t = 0; t < nk - 3; ++t) stage(t, IMain{}, IMain{});
-    if (nk >= 3) stage(nk - 3, IMain{}, IT{});
-    stage(nk - 2, IT{}, ILA{});
-    stage(nk - 1, ILA{}, INone{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // LoRA operands landed; all waves done with the ring
-
+    const bool vec_ok = (N & 7) == 0;
     const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
-    // ---- LoRA up-projection: acc += (T / s) LA^T ----------------------------
-    if (R > 0) {
-        const char* Ts = smem + (nk % 3) * C::STAGE;
-        const char* Ls = smem + ((nk + 1) % 3) * C::STAGE;
-        // T / s is dense; it is fed to the same SMFMAC as two exactly-2:4 halves
-        // with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per group):
-        // over channels [16h, 16h+16) of a 32-rank step the even dwords of the
-        // row are positions 0,1 of each group and the odd dwords positions 2,3.
-        // T / s is rounded to bf16 here.  LA supplies the B operand exactly as
-        // W does in the main loop.
-        float inv[4];
+    char* ep = smem + kEpiOff + wave * kEpiWave;
+    auto scaled = [](uint32_t w, float f) { return pack_bf16x2(bf16_lo(w) * f, bf16_hi(w) * f); };
+
+    int v = blockIdx.x;
+    {
+        int tm, tn;
+        tile_of(v, tiles_m, tiles_n, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    }
+    set_tile_offsets(m0, n0);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, uint32_t(cur), k);  // first tile's stage 0
+
+    for (; v < ntiles; v += gridDim.x) {
+        // stage 0 of this tile is in flight into slot `cur`
 #pragma unroll
-        for (int a = 0; a < 4; ++a) inv[a] = 1.0f / s_lds[wm * 128 + 32 * a + r];
-        auto scaled = [](uint32_t w, float f) {
-            return pack_bf16x2(bf16_lo(w) * f, bf16_hi(w) * f);
-        };
-        for (int ks = 0; ks < (R + 31) / 32; ++ks) {
-            const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
-            const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128), ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
-            bf16x16 bl[4];
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const int row = (wn * 128 + 32 * b + r) * 128;
-                const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
-                const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
-                bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13,
-                                                14, 15);
+            for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+        for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, uint32_t(nxt), k);
+        if (nk > 2) {
+            for (int i = 0; i < kHalf; ++i) dma_grp(IMain{}, 2, aft, 0, i);
+            wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
+        } else {
+            for (int i = 0; i < kHalf; ++i) dma_grp(IT{}, 2, aft, 0, i);
+            if (R > 0) {
+                wait_vmcnt<C::DMA_PER_STAGE + kLoraHalf + 1>();
+            } else {
+                wait_vmcnt<C::DMA_PER_STAGE + 1>();
             }
+        }
+        block_barrier();
+#pragma unroll
+        for (int n = 0; n < 16; ++n) read_n(cur, 0, fr[0], n);
+
+        for (int t = 0; t < nk - 3; ++t) stage(t, IMain{}, IMain{});
+        if (nk >= 3) stage(nk - 3, IMain{}, IT{});
+        stage(nk - 2, IT{}, ILA{});
+        // the current tile's stage loads are all issued: point the offsets at
+        // the next tile, whose stage 0 goes out from here on
+        const int vn = v + gridDim.x;
+        has_next = vn < ntiles;
+        int m0n = m0, n0n = n0;
+        if (has_next) {
+            int tm, tn;
+            tile_of(vn, tiles_m, tiles_n, tm, tn);
+            m0n = tm * BM;
+            n0n = tn * BN;
+            set_tile_offsets(m0n, n0n);
+        }
+        stage(nk - 1, ILA{}, INext0{});
+        // rotation after the last stage: cur = T, nxt = LA, aft = next stage 0
+        for (int i = 0; i < kHalf; ++i) dma_grp(INext0{}, 0, aft, 1, i);
+        if (has_next) {
+            wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();  // LA landed (next stage 0 may fly)
+        } else {
+            wait_vmcnt_lgkm0<0>();
+        }
+        __syncthreads();  // LoRA operands landed; all waves done with the stage slots
+
+        // ---- LoRA up-projection: acc += (T / s) LA^T ------------------------
+        if (R > 0) {
+            const char* Ts = smem + cur;
+            const char* Ls = smem + nxt;
+            // T / s is dense; it is fed to the same SMFMAC as two exactly-2:4
+            // halves with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per
+            // group): over channels [16h, 16h+16) of a 32-rank step the even
+            // dwords of the row are positions 0,1 of each group and the odd
+            // dwords positions 2,3.  T / s is rounded to bf16 here.  LA supplies
+            // the B operand exactly as W does in the main loop.
+            float inv[4];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
-                const int row = (wm * 128 + 32 * a + r) * 128;
-                const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
-                const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
-                const float f = inv[a];
-                const bf16x8 te = __builtin_bit_cast(
-                    bf16x8, u32x4{scaled(t0.x, f), scaled(t0.z, f), scaled(t1.x, f), scaled(t1.z, f)});
-                const bf16x8 to = __builtin_bit_cast(
-                    bf16x8, u32x4{scaled(t0.y, f), scaled(t0.w, f), scaled(t1.y, f), scaled(t1.w, f)});
+                const float sv = s_lds[wm * 128 + 32 * a + r];  // 0 for rows past M
+                inv[a] = sv > 0.f ? 1.0f / sv : 0.f;
+            }
+            for (int ks = 0; ks < (R + 31) / 32; ++ks) {
+                const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
+                const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128);
+                const int ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
+                bf16x16 bl[4];
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
-                    acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(te, bl[b], acc[a][b],
-                                                                          0x4444, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(to, bl[b], acc[a][b],
-                                                                          0xEEEE, 0, 0);
+                    const int row = (wn * 128 + 32 * b + r) * 128;
+                    const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
+                    const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
+                    bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                                    12, 13, 14, 15);
                 }
-            }
-        }
-    }
-
-    // ---- epilogue: y = s * acc, bf16, 16 rows at a time through LDS ---------
-    // rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4; the
-    // half p = 0 / 1 (e < 8 / e >= 8) covers rows 0..15 / 16..31.
-    // scratch in the slot the LoRA operands left free
-    char* ep = smem + ((nk + 2) % 3) * C::STAGE + wave * 4096;  // 16 rows x 128 cols bf16
-    const bool vec_ok = (N & 7) == 0;
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
+                for (int a = 0; a < 4; ++a) {
+                    const int row = (wm * 128 + 32 * a + r) * 128;
+                    const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
+                    const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
+                    const float f = inv[a];
+                    const bf16x8 te = __builtin_bit_cast(
+                        bf16x8,
+                        u32x4{scaled(t0.x, f), scaled(t0.z, f), scaled(t1.x, f), scaled(t1.z, f)});
+                    const bf16x8 to = __builtin_bit_cast(
+                        bf16x8,
+                        u32x4{scaled(t0.y, f), scaled(t0.w, f), scaled(t1.y, f), scaled(t1.w, f)});
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int rbase = wm * 128 + 32 * a + 16 * p;  // tile row of local row 0
-            const f32x4 sA = *reinterpret_cast<const f32x4*>(s_lds + rbase + 4 * h);
-            const f32x4 sB = *reinterpret_cast<const f32x4*>(s_lds + rbase + 8 + 4 * h);
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-#pragma unroll
-                for (int e2 = 0; e2 < 8; ++e2) {
-                    const int lr = 8 * (e2 / 4) + 4 * h + (e2 % 4);  // local row 0..15
-                    const float sv = e2 < 4 ? sA[e2 % 4] : sB[e2 % 4];
-                    *reinterpret_cast<uint16_t*>(ep + lr * 256 + (32 * b + r) * 2) =
-                        __builtin_bit_cast(uint16_t,
-                                           static_cast<__bf16>(sv * acc[a][b][8 * p + e2]));
-                }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int orow = m0 + rbase + (lane >> 2);
-            const int ocol = n0 + wn * 128 + (lane & 3) * 32;
-            if (orow < M) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const u32x4 v = lds_read<u32x4>(ep, (lane >> 2) * 256 + (lane & 3) * 64 + 16 * i);
-                    const int col = ocol + 8 * i;
-                    uint16_t* dst = Y + size_t(orow) * size_t(N) + col;
-                    if (vec_ok && col + 8 <= N) {
-                        *reinterpret_cast<u32x4*>(dst) = v;
-                    } else {
-                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int q2 = 0; q2 < 8; ++q2)
-                            if (col + q2 < N) dst[q2] = uint16_t(w[q2 >> 1] >> (16 * (q2 & 1)));
+                    for (int b = 0; b < 4; ++b) {
+                        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                            te, bl[b], acc[a][b], 0x4444, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                            to, bl[b], acc[a][b], 0xEEEE, 0, 0);
                     }
                 }
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
+
+        // ---- epilogue: y = s * acc, bf16, 8 rows at a time through LDS ------
+        // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
+        // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
+        // Staging rows 4..7 have their 128-byte halves swapped so the two
+        // halves of the wave write different banks.
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + rbase + 4 * h);
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int lr = 4 * h + i;  // staging row 0..7
+                        *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
+                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(sv[i] * acc[a][b][4 * j + i]));
+                    }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
+                const int srow = lane >> 3;
+                const int orow = m0 + rbase + srow;
+                const int ocol = n0 + wn * 128 + (lane & 7) * 16;
+                if (orow < M) {
+                    const int sb = srow * 256 + (((lane & 7) * 32) ^ ((srow >> 2) << 7));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
+                        const int col = ocol + 8 * i;
+                        uint16_t* dst = Y + size_t(orow) * size_t(N) + col;
+                        if (vec_ok && col + 8 <= N) {
+                            *reinterpret_cast<u32x4*>(dst) = w4;
+                        } else {
+                            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                            for (int q2 = 0; q2 < 8; ++q2)
+                                if (col + q2 < N) dst[q2] = uint16_t(w[q2 >> 1] >> (16 * (q2 & 1)));
+                        }
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+        __syncthreads();  // T / LA slots, s and the staging rows are free
+        // the next tile: its stage 0 is in slot `aft`
+        const int t_slot = cur;
+        cur = aft;
+        aft = nxt;
+        nxt = t_slot;
+        m0 = m0n;
+        n0 = n0n;
     }
 }
 
@@ -657,8 +727,12 @@ lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta
                                      const float* scale, const uint16_t* T, const uint16_t* W,
                                      const uint16_t* LA, uint16_t* Y, int M, int N, int K, int R,
                                      hipStream_t stream) {
+    // persistent: one workgroup per compute unit (the kernel's LDS allows one)
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_sparse32, dim3(tiles), dim3(NT), 0, stream, values, meta, scale, T, W,
+    int cus = 0;
+    if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
+    const int grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL(gemm_sparse32, dim3(grid), dim3(NT), 0, stream, values, meta, scale, T, W,
                        LA, Y, M, N, K, R);
     return launch_status();
 }

@@ -11,6 +11,7 @@ namespace lynx {
 namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cu_count[kMaxDevices];    // 0 unknown
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxElems = int64_t(1) << 31;
@@ -61,6 +62,25 @@ lynx_status check_device() {
         g_arch_state[dev].store(st, std::memory_order_relaxed);
     }
     return st == 1 ? LYNX_OK : LYNX_ERR_UNSUPPORTED_DEVICE;
+}
+
+lynx_status device_cu_count(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return LYNX_ERR_DEVICE;
+    }
+    int n = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0) {
+            (void)hipGetLastError();
+            return LYNX_ERR_DEVICE;
+        }
+        g_cu_count[dev].store(n, std::memory_order_relaxed);
+    }
+    *cus = n;
+    return LYNX_OK;
 }
 
 }  // namespace lynx

@@ -18,6 +18,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // Checks that the current device is gfx950 (cached per device ordinal).
 lynx_status check_device();
 
+// Number of compute units of the current device (cached per device ordinal).
+lynx_status device_cu_count(int* cus);
+
 // Maps the last HIP launch error to a status.
 inline lynx_status launch_status() {
     return hipGetLastError() == hipSuccess ? LYNX_OK : LYNX_ERR_DEVICE;
