@@ -9,6 +9,8 @@ from ._abi import (  # noqa: F401
     LynxError,
     lib,
     linear_dense,
+    linear_sequence,
+    sequence_workspace_bytes,
     linear_sparse_lora,
     linear_sparse_lora_packed,
     sparsify,

@@ -21,8 +21,20 @@ STATUS_NAMES = {
     4: "LYNX_ERR_WORKSPACE", 5: "LYNX_ERR_DEVICE", 6: "LYNX_ERR_UNSUPPORTED_DEVICE",
 }
 
+LAYER_SPARSE_LORA, LAYER_DENSE = 0, 1
+
+
+class Layer(ctypes.Structure):
+    """struct lynx_layer (include/lynx.h)."""
+    _fields_ = [("X", ctypes.c_void_p), ("W", ctypes.c_void_p), ("LA", ctypes.c_void_p),
+                ("LB", ctypes.c_void_p), ("Y", ctypes.c_void_p), ("M", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("R", ctypes.c_int64),
+                ("mode", ctypes.c_int32)]
+
+
 # every symbol the public headers declare, with (restype, argtypes)
 _P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_LP = ctypes.POINTER(Layer)
 SIGNATURES = {
     "lynx_status_string": (ctypes.c_char_p, [_I]),
     "lynx_version": (_I, []),
@@ -32,6 +44,8 @@ SIGNATURES = {
     "lynx_linear_sparse_lora_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                             _P]),
     "lynx_linear_dense": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "lynx_sequence_workspace_bytes": (_SZ, [_LP, _I64]),
+    "lynx_linear_sequence": (_I, [_LP, _I64, _P, _SZ, _P]),
     "lynx_probe_mfma": (_I, [_I, _I, _P, _P, _P, _P, _P]),
 }
 
@@ -199,6 +213,45 @@ def linear_dense(X, W, Y=None):
     _check(lib().lynx_linear_dense(_ptr(X), _ptr(W), _ptr(Y), M, N, K, _stream(X.device)),
            "lynx_linear_dense")
     return Y
+
+
+def _layer_struct(d: dict) -> Layer:
+    X, W, Y = d["X"], d["W"], d["Y"]
+    M, K = X.shape
+    N = W.shape[0]
+    dense = d.get("dense", False)
+    LA, LB = (None, None) if dense else (d.get("LA"), d.get("LB"))
+    R = 0 if LA is None else LA.shape[1]
+    _need(X, torch.bfloat16, (M, K), "X")
+    _need(W, torch.bfloat16, (N, K), "W")
+    _need(Y, torch.bfloat16, (M, N), "Y")
+    if R > 0:
+        _need(LA, torch.bfloat16, (N, R), "LA")
+        _need(LB, torch.bfloat16, (R, K), "LB")
+    return Layer(_ptr(X), _ptr(W), _ptr(LA), _ptr(LB), _ptr(Y), M, N, K, R,
+                 LAYER_DENSE if dense else LAYER_SPARSE_LORA)
+
+
+def sequence_workspace_bytes(layers: list) -> int:
+    arr = (Layer * len(layers))(*[_layer_struct(d) for d in layers])
+    return lib().lynx_sequence_workspace_bytes(arr, len(layers))
+
+
+def linear_sequence(layers: list, workspace=None):
+    """Runs the layers in order (lynx_linear_sequence).  Each layer is a dict
+    with X, W, Y (device tensors), LA and LB for a sparse + LoRA layer, and
+    dense=True for a skipped (dense) layer."""
+    if not layers:
+        return
+    arr = (Layer * len(layers))(*[_layer_struct(d) for d in layers])
+    dev = layers[0]["X"].device
+    nbytes = lib().lynx_sequence_workspace_bytes(arr, len(layers))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty((nbytes,), dtype=torch.uint8, device=dev)
+    _check(lib().lynx_linear_sequence(arr, len(layers), _ptr(workspace),
+                                      0 if workspace is None else workspace.numel(),
+                                      _stream(dev)),
+           "lynx_linear_sequence")
 
 
 def probe_mfma(which: int, abid: int, a: torch.Tensor, b: torch.Tensor,

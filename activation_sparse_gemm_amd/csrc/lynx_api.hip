@@ -146,43 +146,137 @@ lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t
                               static_cast<hipStream_t>(stream));
 }
 
-lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
-                                    const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N,
-                                    int64_t K, int64_t R, void* workspace,
-                                    size_t workspace_bytes, lynx_stream_t stream) {
+namespace {
+// Argument checks of the sparse layer; LYNX_OK with *noop set for M or N == 0.
+lynx_status validate_sparse(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                            const uint16_t* LB, const uint16_t* Y, int64_t M, int64_t N,
+                            int64_t K, int64_t R, const void* workspace, size_t workspace_bytes,
+                            bool* noop) {
+    *noop = false;
     if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
-    if (M == 0 || N == 0) return LYNX_OK;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return LYNX_OK;
+    }
     if (!X || !W || !Y) return LYNX_ERR_NULL;
     if (R > 0 && (!LA || !LB)) return LYNX_ERR_NULL;
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
     if (R > 0 && (!aligned16(LA) || !aligned16(LB))) return LYNX_ERR_ALIGN;
-    const WorkspaceLayout L = layout_for(M, K, R);
-    if (!workspace || workspace_bytes < L.total) return LYNX_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < layout_for(M, K, R).total) return LYNX_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LYNX_ERR_ALIGN;
-    lynx_status st = check_device();
-    if (st != LYNX_OK) return st;
+    return LYNX_OK;
+}
+
+lynx_status validate_dense(const uint16_t* X, const uint16_t* W, const uint16_t* Y, int64_t M,
+                           int64_t N, int64_t K, bool* noop) {
+    *noop = false;
+    if (!dims_ok(M, N, K)) return LYNX_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return LYNX_OK;
+    }
+    if (!X || !W || !Y) return LYNX_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
+    return LYNX_OK;
+}
+
+// the sparse layer on validated arguments
+lynx_status run_sparse(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                       const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K, int64_t R,
+                       void* workspace, hipStream_t s) {
+    const WorkspaceLayout L = layout_for(M, K, R);
     char* ws = static_cast<char*>(workspace);
     uint16_t* values = reinterpret_cast<uint16_t*>(ws + L.values);
     uint8_t* meta = reinterpret_cast<uint8_t*>(ws + L.meta);
     float* scale = reinterpret_cast<float*>(ws + L.scale);
     uint16_t* T = R > 0 ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values, meta, scale, T,
-                         s);
+    lynx_status st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values,
+                                     meta, scale, T, s);
     if (st != LYNX_OK) return st;
     return launch_gemm_sparse(values, meta, scale, T, W, R > 0 ? LA : nullptr, Y, int(M), int(N),
                               int(K), int(R), s);
 }
+}  // namespace
+
+lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                                    const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N,
+                                    int64_t K, int64_t R, void* workspace,
+                                    size_t workspace_bytes, lynx_stream_t stream) {
+    bool noop = false;
+    lynx_status st = validate_sparse(X, W, LA, LB, Y, M, N, K, R, workspace, workspace_bytes,
+                                     &noop);
+    if (st != LYNX_OK || noop) return st;
+    st = check_device();
+    if (st != LYNX_OK) return st;
+    return run_sparse(X, W, LA, LB, Y, M, N, K, R, workspace, static_cast<hipStream_t>(stream));
+}
 
 lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
                               int64_t N, int64_t K, lynx_stream_t stream) {
-    if (!dims_ok(M, N, K)) return LYNX_ERR_SHAPE;
-    if (M == 0 || N == 0) return LYNX_OK;
-    if (!X || !W || !Y) return LYNX_ERR_NULL;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
-    lynx_status st = check_device();
+    bool noop = false;
+    lynx_status st = validate_dense(X, W, Y, M, N, K, &noop);
+    if (st != LYNX_OK || noop) return st;
+    st = check_device();
     if (st != LYNX_OK) return st;
     return launch_gemm_dense(X, W, Y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
+}
+
+size_t lynx_sequence_workspace_bytes(const lynx_layer* layers, int64_t n) {
+    if (n < 0 || (n > 0 && !layers)) return 0;
+    size_t need = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const lynx_layer& L = layers[i];
+        if (L.mode == LYNX_LAYER_DENSE) {
+            if (!dims_ok(L.M, L.N, L.K)) return 0;
+        } else if (L.mode == LYNX_LAYER_SPARSE_LORA) {
+            if (!dims_ok(L.M, L.N, L.K) || !rank_ok(L.R)) return 0;
+            if (L.M > 0 && L.N > 0) {
+                const size_t b = layout_for(L.M, L.K, L.R).total;
+                if (b > need) need = b;
+            }
+        } else {
+            return 0;
+        }
+    }
+    return need;
+}
+
+lynx_status lynx_linear_sequence(const lynx_layer* layers, int64_t n, void* workspace,
+                                 size_t workspace_bytes, lynx_stream_t stream) {
+    if (n < 0) return LYNX_ERR_SHAPE;
+    if (n == 0) return LYNX_OK;
+    if (!layers) return LYNX_ERR_NULL;
+    bool any = false;
+    for (int64_t i = 0; i < n; ++i) {
+        const lynx_layer& L = layers[i];
+        bool noop = false;
+        lynx_status st;
+        if (L.mode == LYNX_LAYER_DENSE) {
+            st = validate_dense(L.X, L.W, L.Y, L.M, L.N, L.K, &noop);
+        } else if (L.mode == LYNX_LAYER_SPARSE_LORA) {
+            st = validate_sparse(L.X, L.W, L.LA, L.LB, L.Y, L.M, L.N, L.K, L.R, workspace,
+                                 workspace_bytes, &noop);
+        } else {
+            st = LYNX_ERR_SHAPE;
+        }
+        if (st != LYNX_OK) return st;
+        any = any || !noop;
+    }
+    if (!any) return LYNX_OK;
+    lynx_status st = check_device();
+    if (st != LYNX_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int64_t i = 0; i < n; ++i) {
+        const lynx_layer& L = layers[i];
+        if (L.M == 0 || L.N == 0) continue;
+        if (L.mode == LYNX_LAYER_DENSE) {
+            st = launch_gemm_dense(L.X, L.W, L.Y, int(L.M), int(L.N), int(L.K), s);
+        } else {
+            st = run_sparse(L.X, L.W, L.LA, L.LB, L.Y, L.M, L.N, L.K, L.R, workspace, s);
+        }
+        if (st != LYNX_OK) return st;
+    }
+    return LYNX_OK;
 }
 
 }  // extern "C"

@@ -45,6 +45,9 @@ def parse():
                    choices=["tiny", "qkv", "mlp_up", "mlp_down", "block"])
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--sets", type=int, default=3)
+    p.add_argument("--skip", default="",
+                   help="block workload: comma-separated layer names (qkv, attn_out, mlp_up, "
+                        "mlp_down) run as the dense layer (selective layer skipping)")
     p.add_argument("--rounds", type=int, default=7,
                    help="rounds of the interleaved comparison timing")
     p.add_argument("--calls", type=int, default=20,
@@ -220,18 +223,25 @@ def main():
     import torch
 
     import activation_sparse_gemm_amd as lynx
-    from workloads import make_config, make_layer
+    from workloads import BLOCK_LAYER_NAMES, make_config, make_layer
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     layers = make_config(args.workload)   # one layer, or the block's four in sequence
+    skip = [x for x in args.skip.split(",") if x]
+    if skip and args.workload != "block":
+        sys.exit("--skip applies to the block workload")
+    unknown = set(skip) - set(BLOCK_LAYER_NAMES)
+    if unknown:
+        sys.exit(f"--skip: unknown layers {sorted(unknown)}")
+    skipped = [len(layers) > 1 and BLOCK_LAYER_NAMES[j] in skip for j in range(len(layers))]
 
     def to_dev(b):
         return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
 
     # sets[s][j]: device tensors of layer j in input set s (set 0 = the seeded
     # workload itself, the others independent draws of the same shapes)
-    sets = []
+    sets, seq_workspaces = [], []
     for s in range(args.sets):
         row = []
         for j, base in enumerate(layers):
@@ -243,13 +253,20 @@ def main():
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             packed = lynx.sparsify(X, LB)
-            row.append(dict(X=X, W=W, LA=LA, LB=LB, ws=ws, Y=Y, Yd=Yd, packed=packed))
+            row.append(dict(X=X, W=W, LA=LA, LB=LB, ws=ws, Y=Y, Yd=Yd, packed=packed,
+                            dense=skipped[j]))
+        seq_ws = torch.empty((max(lynx.sequence_workspace_bytes(row), 1),), dtype=torch.uint8,
+                             device=dev)
         sets.append(row)
+        seq_workspaces.append(seq_ws)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     S = len(sets)
 
     def step(i):
+        if len(layers) > 1:   # the block: one lynx_linear_sequence call
+            lynx.linear_sequence(sets[i % S], workspace=seq_workspaces[i % S])
+            return
         for d in sets[i % S]:
             lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"], Y=d["Y"],
                                     workspace=d["ws"])
@@ -260,11 +277,15 @@ def main():
 
     def gemm_only(i):
         for d in sets[i % S]:
+            if d["dense"]:
+                continue
             v, m, sc, T = d["packed"]
             lynx.linear_sparse_lora_packed(v, m, sc, T, d["W"], d["LA"], Y=d["Y"])
 
     def sparsify_only(i):
         for d in sets[i % S]:
+            if d["dense"]:
+                continue
             v, m, sc, T = d["packed"]
             lynx.sparsify(d["X"], d["LB"], out=dict(values=v, meta=m, scale=sc, T=T))
 
@@ -285,12 +306,14 @@ def main():
     ms_gemm, ms_k1, ms_torch = med["gemm"], med["sparsify"], med["torch"]
 
     # dense-equivalent flops of a step (all layers)
-    flops = sum(2 * L.M * L.N * L.K + 2 * L.M * L.R * (L.K + L.N) for L in layers)
+    flops = sum(2 * L.M * L.N * L.K + (0 if sk else 2 * L.M * L.R * (L.K + L.N))
+                for L, sk in zip(layers, skipped))
     dense_flops = sum(2 * L.M * L.N * L.K for L in layers)
     tflops = flops / (ms * 1e-3) / 1e12
     # dominant kernel: the 2:4 GEMM; algorithmic flops = products on kept values
     # (M N K/2 multiply-adds) + LoRA up-projection (M R N multiply-adds)
-    k2_alg_flops = sum(L.M * L.N * L.K + 2 * L.M * L.R * L.N for L in layers)
+    k2_alg_flops = sum(L.M * L.N * L.K + 2 * L.M * L.R * L.N
+                       for L, sk in zip(layers, skipped) if not sk)
     k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
     traffic = traffic_for(K2_SRC, args.workload)
     if args.copy_calibration:
@@ -302,13 +325,15 @@ def main():
         del src, dst
     cpu = None if args.no_cpu else cpu_baseline(layers[-1] if len(layers) == 1 else layers[2])
 
-    shapes = [f"{L.name}: X[{L.M}x{L.K}] -> Y[{L.M}x{L.N}]" for L in layers]
+    shapes = [f"{L.name}: X[{L.M}x{L.K}] -> Y[{L.M}x{L.N}]" + (" (skipped: dense)" if sk else "")
+              for L, sk in zip(layers, skipped)]
     kinds = sorted({L.kind for L in layers})
     first = layers[0]
     config = {"workload": f"{args.workload}: " + "; ".join(shapes) +
                           f"; bf16, rank-{first.R} LoRA, {'/'.join(kinds)} activations, "
                           f"{S} rotating input sets",
-              "layers": [{"M": L.M, "K": L.K, "N": L.N, "R": L.R} for L in layers]}
+              "layers": [{"M": L.M, "K": L.K, "N": L.N, "R": L.R, "skipped": sk}
+                         for L, sk in zip(layers, skipped)]}
     if len(layers) == 1:
         config.update({"M": first.M, "K": first.K, "N": first.N, "R": first.R})
     rec = {

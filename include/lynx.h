@@ -143,6 +143,49 @@ lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t
 lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y,
                               int64_t M, int64_t N, int64_t K, lynx_stream_t stream);
 
+/*
+ * A sequence of linear layers, each either sparse + LoRA or dense: the
+ * block-level driver of selective layer skipping (방법론 "핵심 메커니즘",
+ * Selective Layer Skipping; 구현 및 학습 세부: in single-stream blocks some
+ * layers, e.g. Out/OUp, are left out of the sparsification).  A skipped
+ * layer is the original dense layer Y = X W^T (no LoRA branch, which only
+ * corrects the sparse one).
+ */
+typedef enum lynx_layer_mode {
+    LYNX_LAYER_SPARSE_LORA = 0,  /* Y = S(X) W^T + X (LA LB)^T, as lynx_linear_sparse_lora */
+    LYNX_LAYER_DENSE = 1         /* Y = X W^T, as lynx_linear_dense; LA, LB, R ignored */
+} lynx_layer_mode;
+
+typedef struct lynx_layer {
+    const uint16_t* X;   /* [M][K] bf16 */
+    const uint16_t* W;   /* [N][K] bf16 */
+    const uint16_t* LA;  /* [N][R] bf16, NULL iff R == 0 or the layer is dense */
+    const uint16_t* LB;  /* [R][K] bf16, NULL iff R == 0 or the layer is dense */
+    uint16_t* Y;         /* [M][N] bf16 output */
+    int64_t M, N, K, R;
+    int32_t mode;        /* a lynx_layer_mode */
+} lynx_layer;
+
+/*
+ * Bytes of workspace lynx_linear_sequence needs: the largest
+ * lynx_workspace_bytes(M, K, R) over its sparse layers (0 if there are none,
+ * or if any layer is invalid).  layers: host array of n descriptors.
+ */
+size_t lynx_sequence_workspace_bytes(const lynx_layer* layers, int64_t n);
+
+/*
+ * Runs the n layers in order on `stream` (host array of n descriptors; every
+ * pointer inside is a device pointer).  All layers are validated before any
+ * launch; on an error nothing is written and the first failing layer's status
+ * is returned.  workspace: >= lynx_sequence_workspace_bytes(layers, n) bytes,
+ * 256-byte aligned (NULL allowed when no layer is sparse), shared by the
+ * sparse layers one after another, contents on entry irrelevant, clobbered.
+ * n == 0 is a no-op.  Layers must not write an input of a later layer unless
+ * that order is intended: they run exactly in sequence.
+ */
+lynx_status lynx_linear_sequence(const lynx_layer* layers, int64_t n, void* workspace,
+                                 size_t workspace_bytes, lynx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,10 @@ notes of the repository):
      2-3, two groups per byte with the even group in the low nibble.  In
      memory both are stored in tiles of 16 rows x 64 channels (the operand
      tile of one v_smfmac_f32_16x16x64_bf16 step): see tile_rows.
+  7. Selective Layer Skipping (방법론 "핵심 메커니즘"; 구현 및 학습 세부: in
+     single-stream blocks layers such as Out/OUp are left out): a skipped
+     layer is the original dense layer X W^T, without the LoRA branch, which
+     only exists to correct the sparse one.  See linear_sequence.
 
 Everything is computed in fp64 from exactly decoded bf16 inputs.
 """
@@ -261,3 +265,21 @@ def linear_from_packed(values, meta, scale, T_bits, W_bits, LA_bits, K: int) -> 
 def linear_dense(X_bits, W_bits) -> np.ndarray:
     """The dense layer X W^T the speedup is measured against, fp64 [M, N]."""
     return decode_bf16(X_bits) @ decode_bf16(W_bits).T
+
+
+def linear_sequence(layers) -> list:
+    """Outputs of a sequence of layers, each sparse + LoRA or skipped (dense).
+
+    layers: iterable of (X_bits, W_bits, LA_bits, LB_bits, skipped).  A
+    skipped layer is X W^T (reading 7); the others are linear_sparse_lora.
+    The layers are independent: the sequence is the block's linears in order,
+    without the attention and activation functions between them.
+    """
+    out = []
+    for X_bits, W_bits, LA_bits, LB_bits, skipped in layers:
+        if skipped:
+            out.append(linear_dense(X_bits, W_bits))
+        else:
+            out.append(linear_sparse_lora(X_bits, W_bits, LA_bits, LB_bits))
+    return out
+

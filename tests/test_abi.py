@@ -137,3 +137,58 @@ def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _abi.lib()
+
+
+def layers_of(*specs):
+    """ctypes array of lynx_layer from (M, N, K, R, mode) tuples with fake pointers."""
+    arr = (_abi.Layer * len(specs))()
+    for i, (M, N, K, R, mode) in enumerate(specs):
+        arr[i] = _abi.Layer(A, A, A if R else None, A if R else None, B, M, N, K, R, mode)
+    return arr
+
+
+SP, DN = _abi.LAYER_SPARSE_LORA, _abi.LAYER_DENSE
+
+
+def test_sequence_workspace_bytes_is_the_largest_sparse_layer():
+    arr = layers_of((9216, 9216, 3072, 64, SP), (9216, 3072, 3072, 64, DN),
+                    (9216, 12288, 3072, 64, SP), (9216, 3072, 12288, 64, SP))
+    want = max(_abi.workspace_bytes(9216, 3072, 64), _abi.workspace_bytes(9216, 12288, 64))
+    assert _abi.lib().lynx_sequence_workspace_bytes(arr, 4) == want
+    assert _abi.lib().lynx_sequence_workspace_bytes(layers_of((16, 16, 128, 0, DN)), 1) == 0
+    assert _abi.lib().lynx_sequence_workspace_bytes(layers_of((16, 16, 100, 0, DN)), 1) == 0
+    assert _abi.lib().lynx_sequence_workspace_bytes(layers_of((16, 16, 128, 0, 7)), 1) == 0
+
+
+def call_sequence(arr, n=None, ws=B, wsb=1 << 30):
+    return _abi.lib().lynx_linear_sequence(arr, len(arr) if n is None else n, ws, wsb, None)
+
+
+def test_sequence_validation():
+    good = (16, 16, 128, 16, SP)
+    assert call_sequence(layers_of(good), n=0) == OK
+    assert _abi.lib().lynx_linear_sequence(None, 2, B, 1 << 20, None) == NULL
+    assert call_sequence(layers_of(good), n=-1) == SHAPE
+    # the first failing layer's status, whatever the others are
+    assert call_sequence(layers_of(good, (16, 16, 96, 16, SP))) == SHAPE
+    assert call_sequence(layers_of(good, (16, 16, 128, 0, 5))) == SHAPE
+    assert call_sequence(layers_of((16, 16, 128, 16, SP)), ws=None) == WORKSPACE
+    assert call_sequence(layers_of(good), wsb=_abi.workspace_bytes(16, 128, 16) - 1) == WORKSPACE
+    assert call_sequence(layers_of(good), ws=B + 16) == ALIGN
+    arr = layers_of(good, (16, 16, 128, 0, DN))
+    arr[1].X = A + 2
+    assert call_sequence(arr) == ALIGN
+    arr = layers_of(good)
+    arr[0].LA = None
+    assert call_sequence(arr) == NULL
+    # empty layers are no-ops and need no device
+    assert call_sequence(layers_of((0, 16, 128, 16, SP), (16, 0, 128, 0, DN)), ws=None) == OK
+
+
+def test_sequence_without_gpu_reports_unsupported_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
+    # a dense-only sequence needs no workspace
+    assert call_sequence(layers_of((16, 16, 128, 0, DN)), ws=None) == UNSUPPORTED
+    assert call_sequence(layers_of((16, 16, 128, 16, SP), (16, 16, 128, 0, DN))) == UNSUPPORTED

@@ -325,3 +325,27 @@ def test_tiled_storage_offsets_by_hand():
     # padding rows 20..31 of the second block: zero values, meta 0x44
     assert tv[(1 * 3 + 0) * 512 + 4 * 32] == 0 and tm[(1 * 3 + 2) * 128 + 15 * 8] == 0x44
     np.testing.assert_array_equal(orc.untile_rows(orc.tile_rows(vals, K, 0), M, K), vals)
+
+
+# ---- selective layer skipping (oracle reading 7) ----------------------------
+def test_sequence_skipped_layer_is_the_textbook_product():
+    """A skipped layer is X W^T, summed by hand over K; a sparse one equals
+    linear_sparse_lora; the layers do not interact."""
+    rng = np.random.default_rng(7)
+    from workloads.generators import bf16_bits_from_f32
+    X = bf16_bits_from_f32(rng.standard_normal((3, 8)).astype(np.float32))
+    W = bf16_bits_from_f32(rng.standard_normal((5, 8)).astype(np.float32))
+    LA = bf16_bits_from_f32(0.1 * rng.standard_normal((5, 2)).astype(np.float32))
+    LB = bf16_bits_from_f32(0.1 * rng.standard_normal((2, 8)).astype(np.float32))
+    x, w = orc.decode_bf16(X), orc.decode_bf16(W)
+    by_hand = np.array([[sum(x[m, k] * w[n, k] for k in range(8)) for n in range(5)]
+                        for m in range(3)])
+    skipped, sparse = orc.linear_sequence([(X, W, LA, LB, True), (X, W, LA, LB, False)])
+    assert np.array_equal(skipped, by_hand)
+    assert np.array_equal(sparse, orc.linear_sparse_lora(X, W, LA, LB))
+    # dense inputs that are exactly 2-sparse with no LoRA make both modes agree
+    X2 = X.copy()
+    X2[:, 2::4] = 0
+    X2[:, 3::4] = 0
+    a, b = orc.linear_sequence([(X2, W, None, None, True), (X2, W, None, None, False)])
+    assert np.allclose(a, b, rtol=0, atol=1e-12)

@@ -5,6 +5,7 @@ of the layer's arithmetic, so both the CPU oracle's tests and the HIP path's
 tests and benchmark may use it without sharing any part of the method.
 """
 from .generators import (  # noqa: F401
+    BLOCK_LAYER_NAMES,
     CONFIGS,
     LayerInputs,
     bf16_bits_from_f32,
