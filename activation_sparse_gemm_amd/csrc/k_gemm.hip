@@ -1,5 +1,5 @@
 // Tiled GEMM kernels for gfx950: K2 (2:4 sparse MFMA + LoRA, gemm_sparse32)
-// and K3 (dense MFMA baseline, gemm_dense).
+// and K3 (dense MFMA baseline, gemm_dense32).
 //
 // Layer (RT-Lynx page, 코드 예제, second formula; 방법론 "핵심 메커니즘" and
 // "CUDA 커널 최적화": the 2:4 activation goes to the sparse unit, the LoRA
@@ -7,27 +7,30 @@
 //   Y = s * (X~ W^T) + T LA^T = s * (X~ W^T + (T / s) LA^T).
 // The second form lets the LoRA up-projection accumulate into the same fp32
 // accumulators as the sparse product, with one multiply by s per output in the
-// epilogue; T / s is rounded to bf16 once when staged (its share of Y is a few
-// per mille, so that rounding is far below the output's own bf16 rounding).
+// epilogue; T / s is rounded to bf16 once, when its fragments are formed (its
+// share of Y is a few per mille, so that rounding is far below the output's
+// own bf16 rounding).
 //
-// Both kernels: one 256 x 256 output tile per workgroup of 4 waves (2 x 2),
-// each wave 128 x 128 (256 fp32 accumulators per lane, in AGPRs).  Operands
-// move global -> LDS by buffer_load ... lds (no VGPR staging) into a ring of
-// LDS stages:
+// Both kernels are persistent: one workgroup of 4 waves (2 x 2) per compute
+// unit walks 256 x 256 output tiles, each wave 128 x 128 (4 x 4 accumulator
+// tiles of 32 x 32, 256 fp32 per lane).  Operands move global -> LDS by
+// buffer_load ... lds (no VGPR staging) into a ring of LDS stages that runs on
+// from one tile into the next:
 //   sparse: 64 dense channels per stage: packed values 256 x 64 B, meta
 //           256 x 8 B, W 256 x 128 B (50 KB, 1024 matrix-core cycles per
-//           wave); ring of 3 (150 KB), loads issued 2 stages ahead.  The packed
-//           operand is stored in 16-row x 64-channel tiles, so a stage's A side
-//           is 16 contiguous 1 KB value tiles and 16 contiguous 128 B meta
-//           tiles, read as whole 128-byte lines;
+//           wave); ring of 3 (150 KB).  The packed operand is stored in
+//           16-row x 64-channel tiles, so a stage's A side is 16 contiguous
+//           1 KB value tiles and 16 contiguous 128 B meta tiles;
 //   dense:  32 channels per stage: X 256 x 64 B, W 256 x 64 B (32 KB, 1024
-//           cycles); ring of 4 (128 KB), loads issued 3 stages ahead.
+//           cycles); ring of 4 (128 KB).
 // The loads of a stage are waited for with an explicit vmcnt that leaves the
-// later stages' loads in flight, then one s_barrier per stage.  Rows past M or
-// N lie past the end of their buffer resource and are never read (their LDS
-// slots keep stale values, which only reach outputs that are not stored).
-// LDS rows keep their 16-byte chunks XOR-swizzled by row so the fragment reads
-// of 8 (and 16) consecutive lanes hit distinct banks.
+// later stages' loads in flight, then one s_barrier per stage; every load of
+// both kernels is such an LDS-DMA, so the counts are exact.  Rows past M or N
+// lie past the end of their buffer resource and read as zeros (they only reach
+// outputs that are not stored).  LDS rows keep their 16-byte chunks
+// XOR-swizzled by row so the fragment reads of 8 (and 16) consecutive lanes
+// hit distinct banks.  Y is written through a buffer resource (32-bit
+// offsets), 16 bytes per lane, after an 8-row transpose through LDS.
 //
 // Tile order: workgroups are handed to the 8 XCDs round-robin, so ids are
 // remapped to give each XCD a contiguous range of tiles, and tiles are
@@ -45,28 +48,24 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, BN = 256, NT = 256, GROUP_M = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit format
 
+// K2's stage: 64 dense channels of the 256 x 256 tile
 template <bool SPARSE>
 struct Cfg {
-    static constexpr int BK = SPARSE ? 64 : 32;          // dense channels per stage
+    static_assert(SPARSE, "only the sparse kernel uses this configuration");
+    static constexpr int BK = 64;                        // dense channels per stage
     static constexpr int A_ROW = 64;                     // LDS bytes per A row per stage
-    static constexpr int B_ROW = SPARSE ? 128 : 64;      // LDS bytes per B row per stage
+    static constexpr int B_ROW = 128;                    // LDS bytes per B row per stage
     static constexpr int A_BYTES = BM * A_ROW;
-    static constexpr int META_BYTES = SPARSE ? BM * 8 : 0;
+    static constexpr int META_BYTES = BM * 8;
     static constexpr int B_BYTES = BN * B_ROW;
     static constexpr int STAGE = A_BYTES + META_BYTES + B_BYTES;
-    static constexpr int NSTAGE = SPARSE ? 3 : 4;
+    static constexpr int NSTAGE = 3;
     static constexpr int A_DMA = A_BYTES / 1024 / 4;     // 1 KB DMA instructions per wave
     static constexpr int B_DMA = B_BYTES / 1024 / 4;
     static constexpr int M_DMA = META_BYTES / 256 / 4;   // 256 B (dword) DMA instructions
     static constexpr int DMA_PER_STAGE = A_DMA + B_DMA + M_DMA;
-    static constexpr int EPI_OFF = 64 * 1024;            // epilogue scratch, 4 KB per wave
-    static constexpr int SCALE_OFF = NSTAGE * STAGE;     // s of the tile's 256 rows (sparse)
-    static constexpr int LDS = NSTAGE * STAGE + (SPARSE ? BM * 4 : 0);
-    static_assert(LDS >= EPI_OFF + 4 * 4096, "epilogue scratch must fit");
-    static_assert(LDS <= 160 * 1024, "LDS budget");
-    static_assert(NSTAGE >= 3 && NSTAGE <= 4, "ring depth handled by the waits below");
-    static_assert(NSTAGE * STAGE >= 64 * 1024 + 4 * 4096, "LoRA tiles and epilogue scratch");
-    static_assert((NSTAGE - 1) * DMA_PER_STAGE < 64, "vmcnt range");
+    static constexpr int SCALE_OFF = NSTAGE * STAGE;     // s of the tile's 256 rows
+    static_assert(2 * DMA_PER_STAGE < 64, "vmcnt range");
 };
 
 // 16-byte chunk swizzles within 64-byte and 128-byte rows
@@ -128,6 +127,15 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// The lane id, computed afresh where it is called: per-lane constants needed
+// only at tile boundaries are then recomputed there instead of being kept
+// live (and spilled) across the main loop.
+__device__ __forceinline__ int fresh_lane() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 template <typename T>
 __device__ __forceinline__ T lds_read(const char* smem, int off) {
     return *reinterpret_cast<const T*>(smem + off);
@@ -139,154 +147,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
-
-// ---------------------------------------------------------------------------
-// K3: dense bf16 GEMM Y = X W^T with v_mfma_f32_16x16x32_bf16.
-//
-// 256 x 256 tile per workgroup of 4 waves (2 x 2, 128 x 128 each = 8 x 8
-// accumulator tiles of 16 x 16); ring of 4 LDS stages of 32 channels (X and W
-// 256 x 64 B each, swizzled 64-byte rows), loads issued 3 stages ahead.
-// Lane l, r = l % 16, q = l / 16: A = row r, B = column r, channels
-// [8q, 8q+8) of the stage; accumulator = column r, rows 4q .. 4q+3.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT, 1) void gemm_dense(const uint16_t* __restrict__ X,
-                                                     const uint16_t* __restrict__ W,
-                                                     uint16_t* __restrict__ Y, int M, int N,
-                                                     int K) {
-    using C = Cfg<false>;
-    __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 15, q = lane >> 4;
-    const int wm = wave & 1, wn = wave >> 1;
-
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    int tm, tn;
-    tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-
-    // ---- DMA addressing: instruction j of wave w moves rows 16 (w + 4j) + l/4
-    // of the stage (64-byte LDS rows); lane l lands at LDS byte 16 l of the
-    // instruction's 1 KB, its source is the chunk the row's swizzle puts there.
-    const uint32_t lds0 = static_cast<uint32_t>(
-        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
-    const i32x4 rsA = make_rsrc(X, uint32_t(M) * uint32_t(2 * K));
-    const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
-    int voffA[C::A_DMA], voffB[C::B_DMA];
-#pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j) {
-        const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
-        voffA[j] = (m0 + row) * 2 * K + 16 * (ph ^ swz64(row));
-    }
-#pragma unroll
-    for (int j = 0; j < C::B_DMA; ++j) {
-        const int row = 16 * (wave + 4 * j) + (lane >> 2), ph = lane & 3;
-        voffB[j] = (n0 + row) * 2 * K + 16 * (ph ^ swz64(row));
-    }
-
-    // loads of k-stage t into ring slot t % NSTAGE
-    auto issue_stage = [&](int t) {
-        const uint32_t base = lds0 + uint32_t((t % C::NSTAGE) * C::STAGE);
-#pragma unroll
-        for (int j = 0; j < C::A_DMA; ++j) dma16(base + 1024 * (wave + 4 * j), voffA[j], rsA, t * 64);
-#pragma unroll
-        for (int j = 0; j < C::B_DMA; ++j)
-            dma16(base + C::A_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB, t * 64);
-    };
-
-    const int s64 = swz64(r);
-    const int rowA = wm * 128 + r, rowB = wn * 128 + r;
-
-    f32x4 acc[8][8];
-#pragma unroll
-    for (int a = 0; a < 8; ++a)
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int nk = K / C::BK;
-    __builtin_amdgcn_s_waitcnt(0);
-    // prologue: NSTAGE - 1 stages in flight
-#pragma unroll
-    for (int t = 0; t < C::NSTAGE - 1; ++t)
-        if (t < nk) issue_stage(t);
-    if (nk >= C::NSTAGE - 1) {
-        wait_vmcnt<(C::NSTAGE - 2) * C::DMA_PER_STAGE>();
-    } else {
-        __builtin_amdgcn_s_waitcnt(0);
-    }
-    block_barrier();
-
-    for (int t = 0; t < nk; ++t) {
-        if (t + C::NSTAGE - 1 < nk) issue_stage(t + C::NSTAGE - 1);
-        const char* As = smem + (t % C::NSTAGE) * C::STAGE;
-        const char* Bs = As + C::A_BYTES;
-        bf16x8 bfr[8];
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-            bfr[b] = lds_read<bf16x8>(Bs, (rowB + 16 * b) * 64 + 16 * (q ^ s64));
-#pragma unroll
-        for (int a = 0; a < 8; ++a) {
-            const bf16x8 afr = lds_read<bf16x8>(As, (rowA + 16 * a) * 64 + 16 * (q ^ s64));
-#pragma unroll
-            for (int b = 0; b < 8; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(afr, bfr[b], acc[a][b], 0, 0, 0);
-        }
-        if (t + 1 < nk) {
-            // wait for stage t+1; the stages issued after it may stay in flight
-            const int later = min(nk - 2 - t, C::NSTAGE - 2);
-            if (later == C::NSTAGE - 2) {
-                wait_vmcnt<(C::NSTAGE - 2) * C::DMA_PER_STAGE>();
-            } else if (later == 1) {
-                wait_vmcnt<C::DMA_PER_STAGE>();
-            } else {
-                __builtin_amdgcn_s_waitcnt(0);
-            }
-            block_barrier();
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // all waves done with the ring before LDS is reused
-
-    // ---- epilogue: bf16 through LDS, 16 rows at a time, 16-byte stores ------
-    char* ep = smem + C::EPI_OFF + wave * 4096;  // 16 rows x 128 cols bf16
-    const bool vec_ok = (N & 7) == 0;
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-#pragma unroll
-        for (int b = 0; b < 8; ++b)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                *reinterpret_cast<uint16_t*>(ep + (4 * q + e) * 256 + (16 * b + r) * 2) =
-                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][e]));
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        // lane -> row lane/4 of the 16, 32 columns starting at (lane%4)*32
-        const int orow = m0 + wm * 128 + 16 * a + (lane >> 2);
-        const int ocol = n0 + wn * 128 + (lane & 3) * 32;
-        if (orow < M) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 v = lds_read<u32x4>(ep, (lane >> 2) * 256 + (lane & 3) * 64 + 16 * i);
-                const int col = ocol + 8 * i;
-                uint16_t* dst = Y + size_t(orow) * size_t(N) + col;
-                if (vec_ok && col + 8 <= N) {
-                    *reinterpret_cast<u32x4*>(dst) = v;
-                } else {
-                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                    for (int h = 0; h < 8; ++h)
-                        if (col + h < N) dst[h] = uint16_t(w[h >> 1] >> (16 * (h & 1)));
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
-}
 
 // ---------------------------------------------------------------------------
 // K2: Y = s * (X~ W^T + (T / s) LA^T) with v_smfmac_f32_32x32x32_bf16.
@@ -548,6 +408,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     };
 
     const bool vec_ok = (N & 7) == 0;
+    // Y as a buffer: 32-bit offsets (M N < 2^31) keep the store addressing cheap
+    const __amdgpu_buffer_rsrc_t rsY =
+        __builtin_amdgcn_make_buffer_rsrc(Y, 0, int(uint32_t(M) * uint32_t(N) * 2u), kRsrcWord3);
     const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
     char* ep = smem + kEpiOff + wave * kEpiWave;
     auto scaled = [](uint32_t w, float f) { return pack_bf16x2(bf16_lo(w) * f, bf16_hi(w) * f); };
@@ -685,23 +548,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
-                const int srow = lane >> 3;
+                const int el = fresh_lane();
+                const int srow = el >> 3;
                 const int orow = m0 + rbase + srow;
-                const int ocol = n0 + wn * 128 + (lane & 7) * 16;
+                const int ocol = n0 + wn * 128 + (el & 7) * 16;
                 if (orow < M) {
-                    const int sb = srow * 256 + (((lane & 7) * 32) ^ ((srow >> 2) << 7));
+                    const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
                         const int col = ocol + 8 * i;
-                        uint16_t* dst = Y + size_t(orow) * size_t(N) + col;
+                        const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
                         if (vec_ok && col + 8 <= N) {
-                            *reinterpret_cast<u32x4*>(dst) = w4;
+                            __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
                         } else {
                             const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                             for (int q2 = 0; q2 < 8; ++q2)
-                                if (col + q2 < N) dst[q2] = uint16_t(w[q2 >> 1] >> (16 * (q2 & 1)));
+                                if (col + q2 < N)
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
+                                        yoff + 2u * q2, 0, 0);
                         }
                     }
                 }
@@ -718,6 +585,264 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         nxt = t_slot;
         m0 = m0n;
         n0 = n0n;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K3: dense bf16 GEMM Y = X W^T with v_mfma_f32_32x32x16_bf16, built like K2.
+//
+// Persistent workgroups of 4 waves walk 256 x 256 tiles; each wave's 128 x 128
+// is 4 x 4 accumulator tiles of 32 x 32.  Stages of 32 channels (X and W
+// 256 x 64 B each, swizzled 64-byte rows, 32 KB) in a ring of 4 slots; a
+// stage is two 16-channel sub-steps of 16 MFMAs (32 cycles each, 1024 per
+// stage as in K2, with 32 KB instead of 50 KB to move).  Stage u's 8 DMA
+// instructions go out in two halves, the first in stage u - 4's sub-step 1
+// right after the barrier that frees slot u % 4, the second in stage u - 3's
+// sub-step 0.  The ring runs on across tiles: the stages after a tile's last
+// one are the next tile's first four, in flight during the epilogue.  Lane
+// l, r = l % 32, h = l / 32 (pinned by the probe tests): A = row r, B =
+// column r, channels 8h .. 8h+7 of the 16-channel sub-step (16-byte chunk
+// 2 sub + h of the 64-byte LDS row); D as in K2.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict__ X,
+                                                       const uint16_t* __restrict__ W,
+                                                       uint16_t* __restrict__ Y, int M, int N,
+                                                       int K) {
+    constexpr int kRow = 64;                       // LDS bytes per row per stage
+    constexpr int kABytes = BM * kRow, kBBytes = BN * kRow;
+    constexpr int kStage = kABytes + kBBytes;      // 32 KB
+    constexpr int kSlots = 4;
+    constexpr int kDmaA = kABytes / 1024 / 4, kDmaB = kBBytes / 1024 / 4;  // per wave
+    constexpr int kDma = kDmaA + kDmaB;            // 8 per wave and stage
+    constexpr int kHalfD = kDma / 2;
+    constexpr int kEpiOff = kSlots * kStage;
+    constexpr int kEpiWave = 8 * 256;
+    constexpr int kLds = kEpiOff + 4 * kEpiWave;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 31, h = lane >> 5;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int ntiles = tiles_m * tiles_n;
+    const int nk = K / 32;  // >= 4: K is a multiple of 128
+
+    // instruction j of wave w moves rows 16 (w + 4j) + l/4 of a 256-row operand
+    // (64-byte LDS rows); lane l lands at byte 16 l of the instruction's 1 KB,
+    // its source is the chunk the row's swizzle puts there
+    const uint32_t lds0 = static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
+    const i32x4 rsA = make_rsrc(X, uint32_t(M) * uint32_t(2 * K));
+    const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
+    int voffA[kDmaA], voffB[kDmaB];      // current tile
+    auto offsets = [&](int tm0, int tn0, int* oa, int* ob) {
+        const int l = fresh_lane();
+#pragma unroll
+        for (int j = 0; j < kDmaA; ++j) {
+            const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
+            oa[j] = (tm0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+        }
+#pragma unroll
+        for (int j = 0; j < kDmaB; ++j) {
+            const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
+            ob[j] = (tn0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+        }
+    };
+    // DMA instruction k (0..7) of stage t (of the tile whose offsets are oa/ob)
+    auto dma = [&](const int* oa, const int* ob, int t, int soff, int k) {
+        const uint32_t base = lds0 + uint32_t(soff);
+        if (k < kDmaA) {
+            dma16(base + 1024 * (wave + 4 * k), oa[k], rsA, t * kRow);
+        } else {
+            const int j = k - kDmaA;
+            dma16(base + kABytes + 1024 * (wave + 4 * j), ob[j], rsB, t * kRow);
+        }
+    };
+
+    const int s64 = swz64(r);
+    const int offA = (wm * 128 + r) * kRow;   // + a * 2048
+    const int offB = (wn * 128 + r) * kRow;   // + b * 2048
+    struct Frags {
+        bf16x8 a[4], b[4];
+    };
+    Frags fr[2];
+    // read n (0..7) of a set: A0, B0, A1, A2, A3, B1, B2, B3 (consumption order)
+    auto read_n = [&](int soff, int sub, Frags& f, int n) {
+        constexpr int isb[8] = {0, 1, 0, 0, 0, 1, 1, 1};
+        constexpr int blk[8] = {0, 0, 1, 2, 3, 1, 2, 3};
+        const char* As = smem + soff;
+        const int c = 16 * ((2 * sub + h) ^ s64);
+        if (isb[n]) {
+            f.b[blk[n]] = lds_read<bf16x8>(As + kABytes, offB + blk[n] * 2048 + c);
+        } else {
+            f.a[blk[n]] = lds_read<bf16x8>(As, offA + blk[n] * 2048 + c);
+        }
+    };
+    f32x16 acc[4][4];
+    auto mma = [&](const Frags& f, int k) {
+        const int a = k & 3, b = k >> 2;
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[a], f.b[b], acc[a][b], 0, 0, 0);
+    };
+
+    bool has_next = false;
+    int m0n = 0, n0n = 0;
+    // instruction i of half `half` of stage u: of this tile if u < nk, else of
+    // the next tile (stage u - nk; nothing after the last tile).  The next
+    // tile's offsets are formed on the fly: this only runs in the last stages.
+    auto dma_u = [&](auto main_c, int u, int soff, int half, int i) {
+        constexpr bool MAIN = decltype(main_c)::value;
+        const int k = half * kHalfD + i;
+        if (MAIN || u < nk) {
+            dma(voffA, voffB, u, soff, k);
+        } else if (has_next) {
+            const int j = k < kDmaA ? k : k - kDmaA;
+            const int l = fresh_lane();
+            const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
+            const int off = ((k < kDmaA ? m0n : n0n) + row) * 2 * K + 16 * (ph ^ swz64(row));
+            dma16(lds0 + uint32_t(soff) + (k < kDmaA ? 0 : kABytes) + 1024 * (wave + 4 * j), off,
+                  k < kDmaA ? rsA : rsB, (u - nk) * kRow);
+        }
+    };
+
+    int sl[kSlots] = {0, kStage, 2 * kStage, 3 * kStage};  // slots of stages t .. t+3
+    // one stage; MAIN: every load it issues belongs to this tile (t + 4 < nk);
+    // WAIT = DMA instructions issued after stage t + 1's last
+    auto stage = [&](int t, auto main_c, int wait) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            mma(fr[0], k);
+            if (k < 8) read_n(sl[0], 1, fr[1], k);
+            if (k >= 8 && k - 8 < kHalfD) dma_u(main_c, t + 3, sl[3], 1, k - 8);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            mma(fr[1], k);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (wait >= 16) {
+            wait_vmcnt_lgkm0<16>();
+        } else if (wait >= 8) {
+            wait_vmcnt_lgkm0<8>();
+        } else {
+            wait_vmcnt_lgkm0<0>();
+        }
+        block_barrier();
+#pragma unroll
+        for (int k = 4; k < 16; ++k) {
+            mma(fr[1], k);
+            if (k < 12) read_n(sl[1], 0, fr[0], k - 4);
+            if (k - 4 < kHalfD) dma_u(main_c, t + 4, sl[0], 0, k - 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const int freed = sl[0];
+        sl[0] = sl[1];
+        sl[1] = sl[2];
+        sl[2] = sl[3];
+        sl[3] = freed;
+    };
+
+    const bool vec_ok = (N & 7) == 0;
+    const __amdgpu_buffer_rsrc_t rsY =
+        __builtin_amdgcn_make_buffer_rsrc(Y, 0, int(uint32_t(M) * uint32_t(N) * 2u), kRsrcWord3);
+    char* ep = smem + kEpiOff + wave * kEpiWave;
+
+    int v = blockIdx.x;
+    int m0, n0;
+    {
+        int tm, tn;
+        tile_of(v, tiles_m, tiles_n, tm, tn);
+        m0 = tm * BM;
+        n0 = tn * BN;
+    }
+    offsets(m0, n0, voffA, voffB);
+    __builtin_amdgcn_s_waitcnt(0);
+    // first tile: stages 0, 1, 2 and the first half of 3
+    for (int t = 0; t < 3; ++t)
+        for (int k = 0; k < kDma; ++k) dma(voffA, voffB, t, sl[t], k);
+    for (int i = 0; i < kHalfD; ++i) dma(voffA, voffB, 3, sl[3], i);
+
+    for (; v < ntiles; v += gridDim.x) {
+        // stages 0..2 and half of 3 of this tile are in flight
+        const int vn = v + gridDim.x;
+        has_next = vn < ntiles;
+        m0n = m0;
+        n0n = n0;
+        if (has_next) {
+            int tm, tn;
+            tile_of(vn, tiles_m, tiles_n, tm, tn);
+            m0n = tm * BM;
+            n0n = tn * BN;
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+        wait_vmcnt<2 * kDma + kHalfD>();  // stage 0 has landed
+        block_barrier();
+#pragma unroll
+        for (int n = 0; n < 8; ++n) read_n(sl[0], 0, fr[0], n);
+
+        const int nx = has_next ? kDma : 0;  // DMA instructions of a next-tile stage
+        for (int t = 0; t < nk - 4; ++t) stage(t, std::true_type{}, 2 * kDma);
+        // stage t + 1's later loads: stages t + 2 and t + 3, of this tile or the next
+        for (int t = nk - 4; t < nk; ++t)
+            stage(t, std::false_type{}, (t + 2 < nk ? kDma : nx) + (t + 3 < nk ? kDma : nx));
+
+        // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
+        // (the same staging as K2's epilogue, scale 1)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int rbase = wm * 128 + 32 * a + 8 * j;
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int lr = 4 * h + i;
+                        *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
+                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
+                    }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const int el = fresh_lane();
+                const int srow = el >> 3;
+                const int orow = m0 + rbase + srow;
+                const int ocol = n0 + wn * 128 + (el & 7) * 16;
+                if (orow < M) {
+                    const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
+                        const int col = ocol + 8 * i;
+                        const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
+                        if (vec_ok && col + 8 <= N) {
+                            __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
+                        } else {
+                            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                            for (int q2 = 0; q2 < 8; ++q2)
+                                if (col + q2 < N)
+                                    __builtin_amdgcn_raw_buffer_store_b16(
+                                        uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
+                                        yoff + 2u * q2, 0, 0);
+                        }
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+        // the next tile's stages 0..2 and half of 3 are in sl[0..3]
+        m0 = m0n;
+        n0 = n0n;
+        offsets(m0, n0, voffA, voffB);
     }
 }
 
@@ -740,7 +865,10 @@ lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta
 lynx_status launch_gemm_dense_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                     int N, int K, hipStream_t stream) {
     const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-    hipLaunchKernelGGL(gemm_dense, dim3(tiles), dim3(NT), 0, stream, X, W, Y, M, N, K);
+    int cus = 0;
+    if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
+    const int grid = tiles < cus ? tiles : cus;
+    hipLaunchKernelGGL(gemm_dense32, dim3(grid), dim3(NT), 0, stream, X, W, Y, M, N, K);
     return launch_status();
 }
 
