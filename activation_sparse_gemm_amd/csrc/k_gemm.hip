@@ -48,16 +48,18 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 constexpr int BM = 256, BN = 256, NT = 256, GROUP_M = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit format
 
-// K2's stage: 64 dense channels of the 256 x 256 tile
-template <bool SPARSE>
+// K2's stage: 64 dense channels of a 256 x (64 NB) tile (NB = 4 or 3 column
+// blocks of 32 per wave)
+template <int NB>
 struct Cfg {
-    static_assert(SPARSE, "only the sparse kernel uses this configuration");
+    static_assert(NB == 3 || NB == 4, "tile widths 192 and 256");
+    static constexpr int TILE_N = 64 * NB;               // tile columns
     static constexpr int BK = 64;                        // dense channels per stage
     static constexpr int A_ROW = 64;                     // LDS bytes per A row per stage
     static constexpr int B_ROW = 128;                    // LDS bytes per B row per stage
     static constexpr int A_BYTES = BM * A_ROW;
     static constexpr int META_BYTES = BM * 8;
-    static constexpr int B_BYTES = BN * B_ROW;
+    static constexpr int B_BYTES = TILE_N * B_ROW;
     static constexpr int STAGE = A_BYTES + META_BYTES + B_BYTES;
     static constexpr int NSTAGE = 3;
     static constexpr int A_DMA = A_BYTES / 1024 / 4;     // 1 KB DMA instructions per wave
@@ -166,12 +168,15 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //   D = column r, rows 8 (e / 4) + 4 h + e % 4, e = 0..15.
 // The LoRA up-projection runs on the same instruction (see the epilogue).
 // ---------------------------------------------------------------------------
+template <int NB>
 __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta,
     const float* __restrict__ scale, const uint16_t* __restrict__ T,
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ LA,
     uint16_t* __restrict__ Y, int M, int N, int K, int R) {
-    using C = Cfg<true>;
+    using C = Cfg<NB>;
+    constexpr int TN = C::TILE_N;   // tile columns
+    constexpr int WC = 32 * NB;     // columns per wave
     // ring of 3 stages, the tile's s, and the epilogue's staging rows
     constexpr int kEpiOff = C::SCALE_OFF + BM * 4;
     constexpr int kEpiWave = 8 * 256;  // 8 rows x 128 columns bf16 per wave
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const int r = lane & 31, h = lane >> 5;
     const int wm = wave & 1, wn = wave >> 1;
 
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TN - 1) / TN;
     const int ntiles = tiles_m * tiles_n;
 
     // ---- DMA addressing ----------------------------------------------------
@@ -224,7 +229,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             voffM[j] = (tm0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
         }
     };
-    // one of the 14 DMA instructions of a stage (4 value tiles, 2 meta, 8 W)
+    // one of the DMA instructions of a stage (4 value tiles, 2 meta, 2 NB W)
     auto dma_k = [&](int t, uint32_t slot_off, int k) {
         const uint32_t base = lds0 + slot_off;
         if (k < C::A_DMA) {
@@ -240,19 +245,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 
     // ---- fragments ---------------------------------------------------------
     // Two fragment sets (one per 32-channel sub-step) alternate.  SMFMACs run
-    // column-block-major, k = 4 b + a, and a set's 16 LDS reads are issued in
-    // the order that consumes them: A0, B0, A1, A2, A3, B1, B2, B3.
+    // column-block-major, k = 4 b + a, and a set's 8 + 2 NB LDS reads are
+    // issued in the order that consumes them: A0, B0, A1, A2, A3, B1, B2 (, B3).
+    constexpr int kS = 4 * NB;          // SMFMACs per sub-step
+    constexpr int kReads = 8 + 2 * NB;  // LDS reads per fragment set
     const int s64 = swz64(r), s128 = swz128(r);
     const int offA = (wm * 128 + r) * 64;      // + 32 a rows (a * 2048 bytes)
     const int offM = (wm * 128 + r) * 8;       // + a * 256
-    const int offB = (wn * 128 + r) * 128;     // + b * 4096
+    const int offB = (wn * WC + r) * 128;      // + b * 4096
     struct Frags {
         bf16x8 v[4];
         int i[4];
-        bf16x8 blo[4], bhi[4];
+        bf16x8 blo[NB], bhi[NB];
     };
     Frags fr[2];
-    // read n (0..15) of a set, from the ring slot at byte offset soff
+    // read n (0 .. kReads-1) of a set, from the ring slot at byte offset soff
     auto read_n = [&](int soff, int sub, Frags& f, int n) {
         const char* As = smem + soff;
         const char* Bs = As + C::A_BYTES + C::META_BYTES;
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
     auto mma = [&](const Frags& f, int k) {
         const int a = k & 3, b = k >> 2;
         const bf16x16 bv = __builtin_shufflevector(f.blo[b], f.bhi[b], 0, 1, 2, 3, 4, 5, 6, 7, 8,
@@ -312,8 +319,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     // next tile's first loads are in flight during this tile's LoRA and
     // epilogue.
     constexpr int kHalf = C::DMA_PER_STAGE / 2;
-    static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8, "DMA split");
-    constexpr int kLoraHalf = 4;  // T or LA DMA instructions per half of a LoRA stage
+    static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8 && kHalf >= 5, "DMA split");
+    constexpr int kLoraHalf = 4;  // T DMA instructions per half of the T stage
+    constexpr int kLaHalf = NB;   // LA DMA instructions per half of the LA stage
+    // sub-step 0: reads after SMFMACs 0 .. kR2-1, DMAs from SMFMAC kD0 on
+    constexpr int kR2 = kReads / 2;
+    constexpr int kD0 = kR2 < kS - kHalf ? kR2 : kS - kHalf;
+    static_assert(kR2 + 4 <= kS && kHalf + 4 <= kS, "sub-step 1 slots");
     const int nk = K / 64;  // even: K is a multiple of 128
     enum { kMain, kT, kLA, kNext0 };
     int m0 = 0, n0 = 0;
@@ -337,9 +349,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         constexpr int KIND = decltype(kind_c)::value;
         if constexpr (KIND == kMain) {
             dma_k(u, uint32_t(soff), half * kHalf + i);
-        } else if constexpr (KIND == kT || KIND == kLA) {
-            if (i < kLoraHalf && R > 0) dma_lora(KIND == kT, soff, half * kLoraHalf + i);
-            if (KIND == kT && half == 0 && i == kLoraHalf) dma_scale();
+        } else if constexpr (KIND == kT) {
+            if (i < kLoraHalf && R > 0) dma_lora(true, soff, half * kLoraHalf + i);
+            if (half == 0 && i == kLoraHalf) dma_scale();
+        } else if constexpr (KIND == kLA) {
+            if (i < kLaHalf && R > 0) dma_lora(false, soff, half * kLaHalf + i);
         } else {
             if (has_next) dma_k(0, uint32_t(soff), half * kHalf + i);
         }
@@ -357,7 +371,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             }
         } else {
             if (R > 0) {
-                wait_vmcnt_lgkm0<2 * kLoraHalf>();
+                wait_vmcnt_lgkm0<2 * kLaHalf>();
             } else {
                 wait_vmcnt_lgkm0<0>();
             }
@@ -374,14 +388,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     // of stage t + 3 (first half issued here)
     auto stage = [&](int t, auto g2, auto g3) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < kS; ++k) {
             mma(fr[0], k);
-            if (k < 8) {
+            if (k < kR2) {
                 read_n(cur, 1, fr[1], 2 * k);
                 read_n(cur, 1, fr[1], 2 * k + 1);
-            } else if (k - 8 < kHalf) {
-                dma_grp(g2, t + 2, aft, 1, k - 8);
             }
+            if (k >= kD0 && k - kD0 < kHalf) dma_grp(g2, t + 2, aft, 1, k - kD0);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -392,9 +405,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         wait_next(g2);  // stage t + 1 has landed
         block_barrier();
 #pragma unroll
-        for (int k = 4; k < 16; ++k) {
+        for (int k = 4; k < kS; ++k) {
             mma(fr[1], k);
-            if (k < 12) {
+            if (k - 4 < kR2) {
                 read_n(nxt, 0, fr[0], 2 * (k - 4));
                 read_n(nxt, 0, fr[0], 2 * (k - 4) + 1);
             }
@@ -420,7 +433,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         int tm, tn;
         tile_of(v, tiles_m, tiles_n, tm, tn);
         m0 = tm * BM;
-        n0 = tn * BN;
+        n0 = tn * TN;
     }
     set_tile_offsets(m0, n0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
+            for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
         for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, uint32_t(nxt), k);
         if (nk > 2) {
             for (int i = 0; i < kHalf; ++i) dma_grp(IMain{}, 2, aft, 0, i);
@@ -446,7 +459,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
         block_barrier();
 #pragma unroll
-        for (int n = 0; n < 16; ++n) read_n(cur, 0, fr[0], n);
+        for (int n = 0; n < kReads; ++n) read_n(cur, 0, fr[0], n);
 
         for (int t = 0; t < nk - 3; ++t) stage(t, IMain{}, IMain{});
         if (nk >= 3) stage(nk - 3, IMain{}, IT{});
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             int tm, tn;
             tile_of(vn, tiles_m, tiles_n, tm, tn);
             m0n = tm * BM;
-            n0n = tn * BN;
+            n0n = tn * TN;
             set_tile_offsets(m0n, n0n);
         }
         stage(nk - 1, ILA{}, INext0{});
@@ -493,10 +506,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
                 const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128);
                 const int ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
-                bf16x16 bl[4];
+                bf16x16 bl[NB];
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const int row = (wn * 128 + 32 * b + r) * 128;
+                for (int b = 0; b < NB; ++b) {
+                    const int row = (wn * WC + 32 * b + r) * 128;
                     const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
                     const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
                     bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
@@ -515,7 +528,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                         bf16x8,
                         u32x4{scaled(t0.y, f), scaled(t0.w, f), scaled(t1.y, f), scaled(t1.w, f)});
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) {
+                    for (int b = 0; b < NB; ++b) {
                         acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
                             te, bl[b], acc[a][b], 0x4444, 0, 0);
                         acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
@@ -537,7 +550,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
                 const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + rbase + 4 * h);
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int lr = 4 * h + i;  // staging row 0..7
@@ -548,11 +561,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
+                // (of the wave's WC columns)
                 const int el = fresh_lane();
                 const int srow = el >> 3;
                 const int orow = m0 + rbase + srow;
-                const int ocol = n0 + wn * 128 + (el & 7) * 16;
-                if (orow < M) {
+                const int ocol = n0 + wn * WC + (el & 7) * 16;
+                if (orow < M && (el & 7) < 2 * NB) {
                     const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -852,13 +866,25 @@ lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta
                                      const float* scale, const uint16_t* T, const uint16_t* W,
                                      const uint16_t* LA, uint16_t* Y, int M, int N, int K, int R,
                                      hipStream_t stream) {
-    // persistent: one workgroup per compute unit (the kernel's LDS allows one)
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    // persistent: one workgroup per compute unit (the kernel's LDS allows one).
+    // Tile width 256 or 192: the one whose rounds of tiles over the compute
+    // units cost less (rounds x width; ties to 256), which removes most of the
+    // idle last round when the 256-wide tiles do not divide evenly.
     int cus = 0;
     if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
-    const int grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL(gemm_sparse32, dim3(grid), dim3(NT), 0, stream, values, meta, scale, T, W,
-                       LA, Y, M, N, K, R);
+    const long tm = (M + BM - 1) / BM;
+    auto tiles_for = [&](int tn) { return tm * ((N + tn - 1) / tn); };
+    auto cost = [&](int tn) { return (tiles_for(tn) + cus - 1) / cus * tn; };
+    const bool narrow = cost(192) < cost(256);
+    const long tiles = tiles_for(narrow ? 192 : 256);
+    const int grid = int(tiles < cus ? tiles : cus);
+    if (narrow) {
+        hipLaunchKernelGGL(gemm_sparse32<3>, dim3(grid), dim3(NT), 0, stream, values, meta, scale,
+                           T, W, LA, Y, M, N, K, R);
+    } else {
+        hipLaunchKernelGGL(gemm_sparse32<4>, dim3(grid), dim3(NT), 0, stream, values, meta, scale,
+                           T, W, LA, Y, M, N, K, R);
+    }
     return launch_status();
 }
 

@@ -49,6 +49,22 @@ def test_linear_sparse_lora_shapes(M, K, N, R):
     check(Y, orc.linear_sparse_lora(L.X, L.W, LA, LB), f"sparse_lora {M}x{K}->{N} R{R}")
 
 
+def test_ragged_wide_tiles_sampled_rows():
+    """Several rounds of 256-wide tiles (the width the launcher keeps when 192
+    would not save a round) with ragged M and N tails; the smaller tiled
+    shapes above run 192-wide tiles."""
+    M, K, N, R = 4046, 640, 12188, 48
+    L = make_layer(M, K, N, "heavy", seed=5, R=R)
+    rows = np.unique(np.concatenate([sample_rows(M, n=24, seed=5), np.arange(M - 40, M)]))
+    say(f"ragged wide tiles M={M} K={K} N={N} R={R}")
+    Y = lynx.linear_sparse_lora(dev(L.X), dev(L.W), dev(L.LA), dev(L.LB))
+    Yd = lynx.linear_dense(dev(L.X), dev(L.W))
+    torch.cuda.synchronize()
+    check(torch.from_numpy(host_f64(Y)[rows]), orc.linear_sparse_lora(L.X[rows], L.W, L.LA, L.LB),
+          "ragged wide sparse_lora")
+    check(torch.from_numpy(host_f64(Yd)[rows]), orc.linear_dense(L.X[rows], L.W), "ragged wide dense")
+
+
 @pytest.mark.parametrize("M,K,N,R", SHAPES[:5] + SHAPES[8:10])
 def test_linear_packed_entry(M, K, N, R):
     """The GEMM half on the oracle's own packed operand."""
