@@ -325,8 +325,8 @@ def main():
         del src, dst
     cpu = None if args.no_cpu else cpu_baseline(layers[-1] if len(layers) == 1 else layers[2])
 
-    shapes = [f"{L.name}: X[{L.M}x{L.K}] -> Y[{L.M}x{L.N}]" + (" (skipped: dense)" if sk else "")
-              for L, sk in zip(layers, skipped)]
+    shapes = [(f"{L.name}: " if len(layers) > 1 else "") + f"X[{L.M}x{L.K}] -> Y[{L.M}x{L.N}]"
+              + (" (skipped: dense)" if sk else "") for L, sk in zip(layers, skipped)]
     kinds = sorted({L.kind for L in layers})
     first = layers[0]
     config = {"workload": f"{args.workload}: " + "; ".join(shapes) +
