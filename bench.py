@@ -55,6 +55,9 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="after timing, run a plain 256 MiB streaming kernel (torch.neg) three "
                         "times, the reference for HBM byte counters")
+    p.add_argument("--summarize-mfma", metavar="SQ_DIR",
+                   help="write profiles/mfma_busy_<workload>.json from a rocprofv3 --pmc run of "
+                        "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE and exit")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into profiles/traffic_<workload>.json")
@@ -199,6 +202,54 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
     return rec
 
 
+# shader engines and SIMDs of the MI355X (8 XCDs x 4 SEs, 256 CUs x 4 SIMDs):
+# SQ_BUSY_CYCLES is summed over the shader engines, SQ_VALU_MFMA_BUSY_CYCLES
+# over every SIMD's matrix core
+N_SE, N_SIMD = 32, 1024
+
+
+def summarize_mfma(sq_dir: str, workload: str) -> dict:
+    """Matrix-core busy fraction per kernel: SQ_VALU_MFMA_BUSY_CYCLES over
+    (kernel cycles x SIMDs), the kernel cycles being SQ_BUSY_CYCLES per shader
+    engine (means per dispatch)."""
+    busy = per_dispatch_kib(sq_dir, "SQ_VALU_MFMA_BUSY_CYCLES")
+    sq = per_dispatch_kib(sq_dir, "SQ_BUSY_CYCLES")
+    grbm = per_dispatch_kib(sq_dir, "GRBM_GUI_ACTIVE")
+    kernels = {}
+    for name, b in busy.items():
+        if b <= 0 or name not in sq:
+            continue
+        cycles = sq[name] / N_SE
+        key = ("gemm_sparse32" if "gemm_sparse32" in name else
+               "gemm_dense32" if "gemm_dense32" in name else
+               "sparsify_kernel" if "sparsify_kernel" in name else
+               "torch.matmul (hipBLASLt " + name[:48] + ")" if "Cijk" in name else name[:60])
+        kernels[key] = {"mfma_busy_cycles": round(b), "sq_busy_cycles": round(sq[name]),
+                        "grbm_gui_active": round(grbm.get(name, 0.0)),
+                        "kernel_cycles": round(cycles),
+                        "mfma_busy": round(b / (cycles * N_SIMD), 4)}
+    rec = {"workload": workload, "kernel_sha": source_sha(K2_SRC), "kernels": kernels,
+           "command": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                      f"-d <dir> -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu --sets 1 "
+                      f"--rounds 1 --calls 3 --workload {workload}"}
+    out = os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
+def mfma_busy_for(kernel_src: str, workload: str):
+    """Matrix-core busy fractions from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha") != source_sha(kernel_src):
+        return None
+    return {k: v["mfma_busy"] for k, v in rec["kernels"].items()}
+
+
 def traffic_for(kernel_src: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
@@ -211,6 +262,9 @@ def traffic_for(kernel_src: str, workload: str):
 
 def main():
     args = parse()
+    if args.summarize_mfma:
+        print(json.dumps(summarize_mfma(args.summarize_mfma, args.workload)))
+        return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, args.workload)))
         return
@@ -362,6 +416,11 @@ def main():
                      "achieved": round(k2_tflops, 2), "peak": PEAK_DENSE_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k2_tflops / PEAK_DENSE_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        # HBM bytes of the profiled K2 launch over its measured time, and the
+        # matrix-core busy fractions of the profiled kernels (rocprofv3
+        # counters committed under profiles/, null once the kernel changed)
+        "k2_hbm_gbps": None if traffic is None else round(traffic / (ms_gemm * 1e-3) / 1e9, 1),
+        "mfma_busy": mfma_busy_for(K2_SRC, args.workload),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))
