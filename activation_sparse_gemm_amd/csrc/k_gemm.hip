@@ -4,12 +4,10 @@
 // Layer (RT-Lynx page, 코드 예제, second formula; 방법론 "핵심 메커니즘" and
 // "CUDA 커널 최적화": the 2:4 activation goes to the sparse unit, the LoRA
 // output is generated and accumulated on chip inside the sparse GEMM):
-//   Y = s * (X~ W^T) + T LA^T = s * (X~ W^T + (T / s) LA^T).
-// The second form lets the LoRA up-projection accumulate into the same fp32
-// accumulators as the sparse product, with one multiply by s per output in the
-// epilogue; T / s is rounded to bf16 once, when its fragments are formed (its
-// share of Y is a few per mille, so that rounding is far below the output's
-// own bf16 rounding).
+//   Y = s * (X~ W^T) + T LA^T.
+// The sparse product accumulates in fp32 registers; its rows are then scaled
+// by s in place and the LoRA up-projection accumulates on top of them, on the
+// same instruction, with T as stored.
 //
 // Both kernels are persistent: one workgroup of 4 waves (2 x 2) per compute
 // unit walks 256 x 256 output tiles, each wave 128 x 128 (4 x 4 accumulator
@@ -151,7 +149,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
-// K2: Y = s * (X~ W^T + (T / s) LA^T) with v_smfmac_f32_32x32x32_bf16.
+// K2: Y = s * (X~ W^T) + T LA^T with v_smfmac_f32_32x32x32_bf16.
 //
 // Each wave's 128 x 128 is 4 x 4 accumulator tiles of 32 x 32 (16 fp32 each).
 // A stage is two 32-channel sub-steps of 16 SMFMACs (32 cycles each).  The
@@ -166,7 +164,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 //   B = column r, channels [8h, 8h+8) and [16+8h, 24+8h): chunks 4 sub + h and
 //     4 sub + 2 + h of the 128-byte LDS row;
 //   D = column r, rows 8 (e / 4) + 4 h + e % 4, e = 0..15.
-// The LoRA up-projection runs on the same instruction (see the epilogue).
+// The LoRA up-projection runs on the same instruction (after the main loop).
 // ---------------------------------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
@@ -426,7 +424,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         __builtin_amdgcn_make_buffer_rsrc(Y, 0, int(uint32_t(M) * uint32_t(N) * 2u), kRsrcWord3);
     const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
     char* ep = smem + kEpiOff + wave * kEpiWave;
-    auto scaled = [](uint32_t w, float f) { return pack_bf16x2(bf16_lo(w) * f, bf16_hi(w) * f); };
 
     int v = blockIdx.x;
     {
@@ -486,23 +483,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
         __syncthreads();  // LoRA operands landed; all waves done with the stage slots
 
-        // ---- LoRA up-projection: acc += (T / s) LA^T ------------------------
+        // ---- y = s * acc + T LA^T: rows scaled by s, then the LoRA up-projection
+        // accumulated on top, with T as stored (no bf16 rounding of T / s)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + wm * 128 + 32 * a + 8 * j + 4 * h);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[a][b][4 * j + i] *= sv[i];
+            }
         if (R > 0) {
             const char* Ts = smem + cur;
             const char* Ls = smem + nxt;
-            // T / s is dense; it is fed to the same SMFMAC as two exactly-2:4
+            // T is dense; it is fed to the same SMFMAC as two exactly-2:4
             // halves with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per
             // group): over channels [16h, 16h+16) of a 32-rank step the even
             // dwords of the row are positions 0,1 of each group and the odd
-            // dwords positions 2,3.  T / s is rounded to bf16 here.  LA supplies
-            // the B operand exactly as W does in the main loop.
-            float inv[4];
+            // dwords positions 2,3.  LA supplies the B operand exactly as W
+            // does in the main loop.
+            const int nks = (R + 31) / 32;  // 1 or 2 (R <= 64)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const float sv = s_lds[wm * 128 + 32 * a + r];  // 0 for rows past M
-                inv[a] = sv > 0.f ? 1.0f / sv : 0.f;
-            }
-            for (int ks = 0; ks < (R + 31) / 32; ++ks) {
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks >= nks) break;
                 const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
                 const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128);
                 const int ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
@@ -520,13 +525,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                     const int row = (wm * 128 + 32 * a + r) * 128;
                     const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
                     const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
-                    const float f = inv[a];
-                    const bf16x8 te = __builtin_bit_cast(
-                        bf16x8,
-                        u32x4{scaled(t0.x, f), scaled(t0.z, f), scaled(t1.x, f), scaled(t1.z, f)});
-                    const bf16x8 to = __builtin_bit_cast(
-                        bf16x8,
-                        u32x4{scaled(t0.y, f), scaled(t0.w, f), scaled(t1.y, f), scaled(t1.w, f)});
+                    const bf16x8 te = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.z, t1.x, t1.z});
+                    const bf16x8 to = __builtin_bit_cast(bf16x8, u32x4{t0.y, t0.w, t1.y, t1.w});
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
                         acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             }
         }
 
-        // ---- epilogue: y = s * acc, bf16, 8 rows at a time through LDS ------
+        // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
         // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
         // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
         // Staging rows 4..7 have their 128-byte halves swapped so the two
@@ -548,14 +548,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
-                const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + rbase + 4 * h);
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int lr = 4 * h + i;  // staging row 0..7
                         *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
-                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(sv[i] * acc[a][b][4 * j + i]));
+                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
                     }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
