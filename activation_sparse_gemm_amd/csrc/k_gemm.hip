@@ -617,17 +617,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 // column r, channels 8h .. 8h+7 of the 16-channel sub-step (16-byte chunk
 // 2 sub + h of the 64-byte LDS row); D as in K2.
 // ---------------------------------------------------------------------------
+template <int NB>
 __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict__ X,
                                                        const uint16_t* __restrict__ W,
                                                        uint16_t* __restrict__ Y, int M, int N,
                                                        int K) {
+    constexpr int TN = 64 * NB;                    // tile columns (256 or 192)
+    constexpr int WC = 32 * NB;                    // columns per wave
+    constexpr int kS = 4 * NB;                     // MFMAs per sub-step
+    constexpr int kReads = 4 + NB;                 // LDS reads per fragment set
     constexpr int kRow = 64;                       // LDS bytes per row per stage
-    constexpr int kABytes = BM * kRow, kBBytes = BN * kRow;
-    constexpr int kStage = kABytes + kBBytes;      // 32 KB
+    constexpr int kABytes = BM * kRow, kBBytes = TN * kRow;
+    constexpr int kStage = kABytes + kBBytes;      // 32 KB (28 KB at NB = 3)
     constexpr int kSlots = 4;
     constexpr int kDmaA = kABytes / 1024 / 4, kDmaB = kBBytes / 1024 / 4;  // per wave
-    constexpr int kDma = kDmaA + kDmaB;            // 8 per wave and stage
-    constexpr int kHalfD = kDma / 2;
+    constexpr int kDma = kDmaA + kDmaB;            // 8 (7) per wave and stage
+    constexpr int kH0 = (kDma + 1) / 2, kH1 = kDma - kH0;  // the two halves of a stage's DMA
+    static_assert(kReads + kH1 <= kS && kReads <= kS - 4 && kH0 <= kS - 4, "stage slots");
     constexpr int kEpiOff = kSlots * kStage;
     constexpr int kEpiWave = 8 * 256;
     constexpr int kLds = kEpiOff + 4 * kEpiWave;
@@ -639,7 +645,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, h = lane >> 5;
     const int wm = wave & 1, wn = wave >> 1;
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TN - 1) / TN;
     const int ntiles = tiles_m * tiles_n;
     const int nk = K / 32;  // >= 4: K is a multiple of 128
 
@@ -677,12 +683,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
 
     const int s64 = swz64(r);
     const int offA = (wm * 128 + r) * kRow;   // + a * 2048
-    const int offB = (wn * 128 + r) * kRow;   // + b * 2048
+    const int offB = (wn * WC + r) * kRow;    // + b * 2048
     struct Frags {
-        bf16x8 a[4], b[4];
+        bf16x8 a[4], b[NB];
     };
     Frags fr[2];
-    // read n (0..7) of a set: A0, B0, A1, A2, A3, B1, B2, B3 (consumption order)
+    // read n (0..kReads-1) of a set: A0, B0, A1, A2, A3, B1, B2 (, B3):
+    // consumption order
     auto read_n = [&](int soff, int sub, Frags& f, int n) {
         constexpr int isb[8] = {0, 1, 0, 0, 0, 1, 1, 1};
         constexpr int blk[8] = {0, 0, 1, 2, 3, 1, 2, 3};
@@ -694,7 +701,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
             f.a[blk[n]] = lds_read<bf16x8>(As, offA + blk[n] * 2048 + c);
         }
     };
-    f32x16 acc[4][4];
+    f32x16 acc[4][NB];
     auto mma = [&](const Frags& f, int k) {
         const int a = k & 3, b = k >> 2;
         acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[a], f.b[b], acc[a][b], 0, 0, 0);
@@ -707,7 +714,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
     // tile's offsets are formed on the fly: this only runs in the last stages.
     auto dma_u = [&](auto main_c, int u, int soff, int half, int i) {
         constexpr bool MAIN = decltype(main_c)::value;
-        const int k = half * kHalfD + i;
+        const int k = half * kH0 + i;
         if (MAIN || u < nk) {
             dma(voffA, voffB, u, soff, k);
         } else if (has_next) {
@@ -725,10 +732,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
     // WAIT = DMA instructions issued after stage t + 1's last
     auto stage = [&](int t, auto main_c, int wait) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < kS; ++k) {
             mma(fr[0], k);
-            if (k < 8) read_n(sl[0], 1, fr[1], k);
-            if (k >= 8 && k - 8 < kHalfD) dma_u(main_c, t + 3, sl[3], 1, k - 8);
+            if (k < kReads) read_n(sl[0], 1, fr[1], k);
+            if (k >= kReads && k - kReads < kH1) dma_u(main_c, t + 3, sl[3], 1, k - kReads);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -736,19 +743,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
             mma(fr[1], k);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (wait >= 16) {
-            wait_vmcnt_lgkm0<16>();
-        } else if (wait >= 8) {
-            wait_vmcnt_lgkm0<8>();
+        if (wait >= 2 * kDma) {
+            wait_vmcnt_lgkm0<2 * kDma>();
+        } else if (wait >= kDma) {
+            wait_vmcnt_lgkm0<kDma>();
         } else {
             wait_vmcnt_lgkm0<0>();
         }
         block_barrier();
 #pragma unroll
-        for (int k = 4; k < 16; ++k) {
+        for (int k = 4; k < kS; ++k) {
             mma(fr[1], k);
-            if (k < 12) read_n(sl[1], 0, fr[0], k - 4);
-            if (k - 4 < kHalfD) dma_u(main_c, t + 4, sl[0], 0, k - 4);
+            if (k - 4 < kReads) read_n(sl[1], 0, fr[0], k - 4);
+            if (k - 4 < kH0) dma_u(main_c, t + 4, sl[0], 0, k - 4);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int freed = sl[0];
@@ -769,14 +776,14 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
         int tm, tn;
         tile_of(v, tiles_m, tiles_n, tm, tn);
         m0 = tm * BM;
-        n0 = tn * BN;
+        n0 = tn * TN;
     }
     offsets(m0, n0, voffA, voffB);
     __builtin_amdgcn_s_waitcnt(0);
     // first tile: stages 0, 1, 2 and the first half of 3
     for (int t = 0; t < 3; ++t)
         for (int k = 0; k < kDma; ++k) dma(voffA, voffB, t, sl[t], k);
-    for (int i = 0; i < kHalfD; ++i) dma(voffA, voffB, 3, sl[3], i);
+    for (int i = 0; i < kH0; ++i) dma(voffA, voffB, 3, sl[3], i);
 
     for (; v < ntiles; v += gridDim.x) {
         // stages 0..2 and half of 3 of this tile are in flight
@@ -788,16 +795,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
             int tm, tn;
             tile_of(vn, tiles_m, tiles_n, tm, tn);
             m0n = tm * BM;
-            n0n = tn * BN;
+            n0n = tn * TN;
         }
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = f32x16{};
-        wait_vmcnt<2 * kDma + kHalfD>();  // stage 0 has landed
+            for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
+        wait_vmcnt<2 * kDma + kH0>();  // stage 0 has landed
         block_barrier();
 #pragma unroll
-        for (int n = 0; n < 8; ++n) read_n(sl[0], 0, fr[0], n);
+        for (int n = 0; n < kReads; ++n) read_n(sl[0], 0, fr[0], n);
 
         const int nx = has_next ? kDma : 0;  // DMA instructions of a next-tile stage
         for (int t = 0; t < nk - 4; ++t) stage(t, std::true_type{}, 2 * kDma);
@@ -813,7 +820,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
             for (int j = 0; j < 4; ++j) {
                 const int rbase = wm * 128 + 32 * a + 8 * j;
 #pragma unroll
-                for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < NB; ++b)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int lr = 4 * h + i;
@@ -826,8 +833,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
                 const int el = fresh_lane();
                 const int srow = el >> 3;
                 const int orow = m0 + rbase + srow;
-                const int ocol = n0 + wn * 128 + (el & 7) * 16;
-                if (orow < M) {
+                const int ocol = n0 + wn * WC + (el & 7) * 16;
+                if (orow < M && (el & 7) < 2 * NB) {
                     const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
@@ -889,11 +896,20 @@ lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta
 
 lynx_status launch_gemm_dense_tiled(const uint16_t* X, const uint16_t* W, uint16_t* Y, int M,
                                     int N, int K, hipStream_t stream) {
-    const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    // persistent, with the same choice of tile width as the sparse kernel
     int cus = 0;
     if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
-    const int grid = tiles < cus ? tiles : cus;
-    hipLaunchKernelGGL(gemm_dense32, dim3(grid), dim3(NT), 0, stream, X, W, Y, M, N, K);
+    const long tm = (M + BM - 1) / BM;
+    auto tiles_for = [&](int tn) { return tm * ((N + tn - 1) / tn); };
+    auto cost = [&](int tn) { return (tiles_for(tn) + cus - 1) / cus * tn; };
+    const bool narrow = cost(192) < cost(256);
+    const long tiles = tiles_for(narrow ? 192 : 256);
+    const int grid = int(tiles < cus ? tiles : cus);
+    if (narrow) {
+        hipLaunchKernelGGL(gemm_dense32<3>, dim3(grid), dim3(NT), 0, stream, X, W, Y, M, N, K);
+    } else {
+        hipLaunchKernelGGL(gemm_dense32<4>, dim3(grid), dim3(NT), 0, stream, X, W, Y, M, N, K);
+    }
     return launch_status();
 }
 

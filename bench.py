@@ -99,43 +99,72 @@ def time_interleaved(fns: dict, rounds: int, calls: int, stream) -> dict:
             end.record(stream)
             torch.cuda.synchronize()
             per[name].append(start.elapsed_time(end) / calls)
-    return {name: statistics.median(v) for name, v in per.items()}
+    def pct(v, q):  # nearest-rank percentile of the per-round averages
+        v = sorted(v)
+        return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+    return {name: (statistics.median(v), pct(v, 0.1), pct(v, 0.9)) for name, v in per.items()}
 
 
-def cpu_baseline(L, min_s=10.0, max_rows_growth=8.0):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(L, min_s=10.0, max_rows_growth=8.0, one_thread_s=6.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload.
 
     The row count grows until one call takes about four seconds or covers the
     whole layer; calls at that size then repeat until min_s seconds of CPU work
-    have been timed.  Each call includes the oracle's own decode of W, LA, LB."""
+    have been timed.  Each call includes the oracle's own decode of W, LA, LB.
+    The same is then repeated with the BLAS pool limited to one thread (about
+    one_thread_s seconds), reported beside it."""
     from oracle import lynx_oracle as orc
     try:
         import threadpoolctl
         info = threadpoolctl.threadpool_info()
         cores = max((i.get("num_threads", 1) for i in info), default=os.cpu_count())
+        blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                                 for i in info if i.get("user_api") == "blas"})) or "unknown"
     except Exception:  # pragma: no cover
-        cores = os.cpu_count()
+        threadpoolctl, cores, blas = None, os.cpu_count(), "unknown"
 
     def run(rows):
         t0 = time.perf_counter()
         orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
         return time.perf_counter() - t0
 
-    rows = min(L.M, 128)
-    dt = run(rows)
-    while dt < 4.0 and rows < L.M:
-        rows = min(L.M, int(rows * min(max_rows_growth, max(2.0, 4.0 / max(dt, 1e-3)))))
+    def measure(target_call_s, budget_s):
+        rows = min(L.M, 16)
         dt = run(rows)
-    total, calls = 0.0, 0
-    while total < min_s:
-        total += run(rows)
-        calls += 1
-    flops = calls * (2 * rows * L.N * L.K + 2 * rows * L.R * (L.K + L.N))
-    return {"value": round(flops / total / 1e12, 6), "unit": "TFLOP/s (dense-equivalent)",
-            "cores": cores, "kind": "oracle", "seconds": round(total, 2),
-            "sample": f"{calls} call(s) on the first {rows} of {L.M} rows of the {L.name} layer "
-                      f"(full W, LA, LB): fp64 NumPy oracle with selection, norms and both "
-                      f"contractions"}
+        while dt < target_call_s and rows < L.M:
+            rows = min(L.M, int(rows * min(max_rows_growth, max(2.0, target_call_s / max(dt, 1e-3)))))
+            dt = run(rows)
+        total, calls = 0.0, 0
+        while total < budget_s:
+            total += run(rows)
+            calls += 1
+        flops = calls * (2 * rows * L.N * L.K + 2 * rows * L.R * (L.K + L.N))
+        return flops / total / 1e12, total, calls, rows
+
+    value, total, calls, rows = measure(4.0, min_s)
+    rec = {"value": round(value, 6), "unit": "TFLOP/s (dense-equivalent)",
+           "cores": cores, "kind": "oracle", "seconds": round(total, 2),
+           "sample": f"{calls} call(s) on the first {rows} of {L.M} rows of the {L.name} layer "
+                     f"(full W, LA, LB): fp64 NumPy oracle with selection, norms and both "
+                     f"contractions",
+           "cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "blas": blas}
+    if threadpoolctl is not None:
+        with threadpoolctl.threadpool_limits(1):
+            v1, t1, c1, r1 = measure(2.0, one_thread_s)
+        rec["one_thread"] = {"value": round(v1, 6), "seconds": round(t1, 2),
+                             "sample": f"{c1} call(s) on the first {r1} rows, BLAS limited to 1 thread"}
+    return rec
 
 
 K2_SRC = os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc", "k_gemm.hip")
@@ -356,8 +385,8 @@ def main():
     med = time_interleaved({"sparse": step, "dense": dense, "gemm": gemm_only,
                             "sparsify": sparsify_only, "torch": torch_mm},
                            rounds=args.rounds, calls=args.calls, stream=stream)
-    ms_sparse_i, ms_dense = med["sparse"], med["dense"]
-    ms_gemm, ms_k1, ms_torch = med["gemm"], med["sparsify"], med["torch"]
+    ms_sparse_i, ms_dense = med["sparse"][0], med["dense"][0]
+    ms_gemm, ms_k1, ms_torch = med["gemm"][0], med["sparsify"][0], med["torch"][0]
 
     # dense-equivalent flops of a step (all layers)
     flops = sum(2 * L.M * L.N * L.K + (0 if sk else 2 * L.M * L.R * (L.K + L.N))
@@ -410,6 +439,8 @@ def main():
         "speedup_vs_torch_matmul": round(ms_torch / ms_sparse_i, 3),
         "interleaved_ms": {"sparse_layer": round(ms_sparse_i, 5), "dense_layer": round(ms_dense, 5),
                            "torch_matmul": round(ms_torch, 5)},
+        # p10 / p90 of the per-round averages behind each median
+        "interleaved_p10_p90_ms": {k: [round(v[1], 5), round(v[2], 5)] for k, v in med.items()},
         "dense_tflops": round(dense_flops / (ms_dense * 1e-3) / 1e12, 2),
         "split_ms": {"sparsify": round(ms_k1, 5), "sparse_gemm_lora": round(ms_gemm, 5)},
         "roofline": {"bound": "mfma", "kernel": "gemm_sparse32 (2:4 SMFMAC + LoRA up-projection)",
