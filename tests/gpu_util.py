@@ -69,7 +69,11 @@ def sample_rows(M: int, n: int = 48, seed: int = 0, tile: int = 256) -> np.ndarr
     return np.array(sorted(p for p in picks if 0 <= p < M))
 
 
-def dump_dir() -> str:
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    os.makedirs(d, exist_ok=True)
+def dump_dir():
+    """Directory for raw probe outputs kept for offline inspection, named by the
+    LYNX_PROBE_DUMP_DIR environment variable; None (nothing is written) when
+    it is unset."""
+    d = os.environ.get("LYNX_PROBE_DUMP_DIR")
+    if d:
+        os.makedirs(d, exist_ok=True)
     return d

@@ -92,7 +92,8 @@ def test_smfmac_16x16x64_layout(abid):
     b_bits, b = bf16_small_ints(rng, (64, 16))
     idx = random_index_words(rng, 64)
     d = run(0, abid, a_bits, b_bits, idx, (64, 4))
-    np.savez(f"{dump_dir()}/probe_s16_{abid}.npz", a=a, b=b, idx=idx, d=d)
+    if dump_dir():
+        np.savez(f"{dump_dir()}/probe_s16_{abid}.npz", a=a, b=b, idx=idx, d=d)
     A = expand_sparse(a, idx, abid, 16, 64, lambda l: l % 16, lambda l: 16 * (l // 16))
     B = np.zeros((64, 16))
     for l in range(64):
@@ -108,7 +109,8 @@ def test_smfmac_32x32x32_layout(abid):
     b_bits, b = bf16_small_ints(rng, (64, 16))
     idx = random_index_words(rng, 64)
     d = run(1, abid, a_bits, b_bits, idx, (64, 16))
-    np.savez(f"{dump_dir()}/probe_s32_{abid}.npz", a=a, b=b, idx=idx, d=d)
+    if dump_dir():
+        np.savez(f"{dump_dir()}/probe_s32_{abid}.npz", a=a, b=b, idx=idx, d=d)
     A = expand_sparse(a, idx, abid, 32, 32, lambda l: l % 32, lambda l: 16 * (l // 32))
     B = np.zeros((32, 32))
     for l in range(64):
