@@ -289,20 +289,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(f.v[a], bv, acc[a][b], f.i[a], 0, 0);
     };
 
-    // Ring schedule.  Stage u's 14 DMA instructions go out in two halves: the
-    // first 7 in stage u - 3's sub-step 1, right after the barrier that frees
-    // slot u % 3, and the other 7 in stage u - 2's sub-step 0.  Per stage t
-    // (set 0 holds sub-step 0's fragments):
-    //   sub-step 0: 16 SMFMACs on set 0; two reads of set 1 (same slot) after
-    //     each of the first 8, one DMA of stage t + 2's second half after each
-    //     of the next 7;
-    //   sub-step 1: 4 SMFMACs on set 1; wait for stage t + 1's loads and this
-    //     wave's reads; barrier (slot t % 3 is free); 12 SMFMACs, the first 8
-    //     each followed by two reads of stage t + 1's set 0 and the first 7 by
-    //     one DMA of stage t + 3's first half into slot t % 3.
+    // Ring schedule.  Stage u's DMA instructions (14 at width 256, 12 at 192)
+    // go out in two halves: the first half starts in stage u - 3's sub-step 1,
+    // after the barrier that frees slot u % 3 (kPartA instructions; the other
+    // kPartB of the first half, when the slots run short, join the second
+    // half), and the second half goes out in stage u - 2's sub-step 0.  Per
+    // stage t (set 0 holds sub-step 0's fragments):
+    //   sub-step 0: SMFMACs on set 0; two reads of set 1 (same slot) after
+    //     each of the first kR2, then the DMAs of stage t + 2 (kPartB + half),
+    //     about one after each remaining SMFMAC;
+    //   sub-step 1: one SMFMAC on set 1; wait for stage t + 1's loads and this
+    //     wave's reads; barrier (slot t % 3 is free); the other SMFMACs, the
+    //     first kR2 each followed by two reads of stage t + 1's set 0, the next
+    //     kPartA by one DMA of stage t + 3's first half into slot t % 3.
     // Every memory instruction sits between two SMFMACs (sched_barrier), so
-    // the matrix core keeps issuing while they are queued, and the last reads
-    // of a set are issued four SMFMACs before the set is first used.
+    // the matrix core keeps issuing while they are queued, and no SMFMAC slot
+    // carries both fragment reads and DMAs: the LDS serves both, and keeping
+    // them apart (with the barrier after the first SMFMAC of sub-step 1
+    // rather than the fourth) took 7% off the cycles of an MLP-up launch.
     // The two stages after a tile's last one carry its LoRA operands through
     // the same slots: "stage" nk is the tile's 256 rows of T and "stage"
     // nk + 1 its 256 rows of LA, 8 DMA instructions each (128-byte rows; ranks
@@ -320,10 +324,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     static_assert(C::DMA_PER_STAGE == 2 * kHalf && kHalf <= 8 && kHalf >= 5, "DMA split");
     constexpr int kLoraHalf = 4;  // T DMA instructions per half of the T stage
     constexpr int kLaHalf = NB;   // LA DMA instructions per half of the LA stage
-    // sub-step 0: reads after SMFMACs 0 .. kR2-1, DMAs from SMFMAC kD0 on
-    constexpr int kR2 = kReads / 2;
-    constexpr int kD0 = kR2 < kS - kHalf ? kR2 : kS - kHalf;
-    static_assert(kR2 + 4 <= kS && kHalf + 4 <= kS, "sub-step 1 slots");
+    constexpr int kR2 = kReads / 2;  // SMFMAC slots with reads, per sub-step
+    constexpr int kBar = 1;          // SMFMACs of sub-step 1 before its wait and barrier
+    // first-half DMAs after sub-step 1's reads; the rest join the second half
+    constexpr int kPartA = kS - kBar - kR2 < kHalf ? kS - kBar - kR2 : kHalf;
+    constexpr int kPartB = kHalf - kPartA;
+    static_assert(kPartA > 0 && kPartB >= 0 && kR2 + kBar <= kS, "stage slots");
     const int nk = K / 64;  // even: K is a multiple of 128
     enum { kMain, kT, kLA, kNext0 };
     int m0 = 0, n0 = 0;
@@ -392,24 +398,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 read_n(cur, 1, fr[1], 2 * k);
                 read_n(cur, 1, fr[1], 2 * k + 1);
             }
-            if (k >= kD0 && k - kD0 < kHalf) dma_grp(g2, t + 2, aft, 1, k - kD0);
+            if (k >= kR2) {
+                // stage t + 2's kPartB + kHalf DMAs over the slots after the reads
+                constexpr int kSlots = kS - kR2;
+#pragma unroll
+                for (int d = k - kR2; d < kPartB + kHalf; d += kSlots) {
+                    if (d < kPartB) {
+                        dma_grp(g2, t + 2, aft, 0, kPartA + d);
+                    } else {
+                        dma_grp(g2, t + 2, aft, 1, d - kPartB);
+                    }
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kBar; ++k) {
             mma(fr[1], k);
             __builtin_amdgcn_sched_barrier(0);
         }
         wait_next(g2);  // stage t + 1 has landed
         block_barrier();
 #pragma unroll
-        for (int k = 4; k < kS; ++k) {
+        for (int k = kBar; k < kS; ++k) {
             mma(fr[1], k);
-            if (k - 4 < kR2) {
-                read_n(nxt, 0, fr[0], 2 * (k - 4));
-                read_n(nxt, 0, fr[0], 2 * (k - 4) + 1);
+            if (k - kBar < kR2) {
+                read_n(nxt, 0, fr[0], 2 * (k - kBar));
+                read_n(nxt, 0, fr[0], 2 * (k - kBar) + 1);
             }
-            if (k - 4 < kHalf) dma_grp(g3, t + 3, cur, 0, k - 4);
+            if (k - kBar - kR2 >= 0 && k - kBar - kR2 < kPartA)
+                dma_grp(g3, t + 3, cur, 0, k - kBar - kR2);
             __builtin_amdgcn_sched_barrier(0);
         }
         const int freed = cur;
@@ -444,14 +462,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
         for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, uint32_t(nxt), k);
         if (nk > 2) {
-            for (int i = 0; i < kHalf; ++i) dma_grp(IMain{}, 2, aft, 0, i);
-            wait_vmcnt<C::DMA_PER_STAGE + kHalf>();  // stage 0 has landed
+            for (int i = 0; i < kPartA; ++i) dma_grp(IMain{}, 2, aft, 0, i);
+            wait_vmcnt<C::DMA_PER_STAGE + kPartA>();  // stage 0 has landed
         } else {
-            for (int i = 0; i < kHalf; ++i) dma_grp(IT{}, 2, aft, 0, i);
+            for (int i = 0; i < kPartA; ++i) dma_grp(IT{}, 2, aft, 0, i);
+            // the T stage's first kPartA instructions: T rows, and s unless it
+            // is in part B
+            constexpr int kScaleA = kPartA > kLoraHalf ? 1 : 0;
+            constexpr int kTA = kPartA < kLoraHalf ? kPartA : kLoraHalf;
             if (R > 0) {
-                wait_vmcnt<C::DMA_PER_STAGE + kLoraHalf + 1>();
+                wait_vmcnt<C::DMA_PER_STAGE + kTA + kScaleA>();
             } else {
-                wait_vmcnt<C::DMA_PER_STAGE + 1>();
+                wait_vmcnt<C::DMA_PER_STAGE + kScaleA>();
             }
         }
         block_barrier();
@@ -475,6 +497,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
         stage(nk - 1, ILA{}, INext0{});
         // rotation after the last stage: cur = T, nxt = LA, aft = next stage 0
+        for (int i = kPartA; i < kHalf; ++i) dma_grp(INext0{}, 0, aft, 0, i);
         for (int i = 0; i < kHalf; ++i) dma_grp(INext0{}, 0, aft, 1, i);
         if (has_next) {
             wait_vmcnt_lgkm0<C::DMA_PER_STAGE>();  // LA landed (next stage 0 may fly)
