@@ -48,6 +48,15 @@ def test_sparsify_shapes(M, K, R):
     check_sparsify(Xb, LB, f"heavy {M}x{K}")
 
 
+@pytest.mark.parametrize("M,R", [(5000, 64), (4120, 48), (8192, 64)])
+def test_sparsify_many_row_blocks(M, R):
+    """More than one round of workgroups on the chip, with ragged and exact M
+    (also guards the packed buffers: a write past them lands in the next
+    output and shows up as a wrong scale)."""
+    Xb = make_activation("heavy", M, 384, seed=M)
+    check_sparsify(Xb, make_weights(8, 384, R, seed=R)[2], f"heavy {M}x384")
+
+
 def test_sparsify_gelu_input():
     Xb = make_activation("gelu", 64, 3072, seed=3)
     check_sparsify(Xb, make_weights(8, 3072, 64, seed=3)[2], "gelu 64x3072")
