@@ -128,22 +128,37 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     double n2 = 0.0, nt2 = 0.0;
 
-    for (int c = wave; c < nchunks; c += nwaves) {
+    // X: the lane's 32 channels of a chunk.  LB: its rows x the chunk's 128
+    // channels, read as whole row segments (instruction j: rows 4j .. 4j+3,
+    // lane l -> row 4j + l / 16, 16-byte piece l % 16), later put in the
+    // wave's LDS area for the MFMA B operand.  A wave walks its chunks one
+    // after another, so each load is issued a chunk ahead: the next chunk's X
+    // before this chunk is worked on, its LB as soon as this chunk's LB has
+    // gone to the LDS (the same registers).
+    auto load_x = [&](int c, u32x4* xd) {
         const int k = c * kChunk + q * 32;
-        u32x4 xv[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[i] = *reinterpret_cast<const u32x4*>(xrow + k + 8 * i);
-
-        // LB rows x this chunk's 128 channels, read as whole row segments
-        // (instruction j: rows 4j .. 4j+3, lane l -> row 4j + l / 16, 16-byte
-        // piece l % 16) and put in the wave's LDS area for the MFMA B operand
-        u32x4 lbraw[RT > 0 ? R / 4 : 1];
+        for (int i = 0; i < 4; ++i) xd[i] = *reinterpret_cast<const u32x4*>(xrow + k + 8 * i);
+    };
+    auto load_lb = [&](int c, u32x4* ld) {
 #pragma unroll
         for (int j = 0; j < (RT > 0 ? R / 4 : 0); ++j) {
             const int lr = 4 * j + (lane >> 4);
-            lbraw[j] = *reinterpret_cast<const u32x4*>(LB + size_t(lr) * size_t(K) +
-                                                       size_t(c) * kChunk + 8 * (lane & 15));
+            ld[j] = *reinterpret_cast<const u32x4*>(LB + size_t(lr) * size_t(K) +
+                                                    size_t(c) * kChunk + 8 * (lane & 15));
         }
+    };
+    u32x4 xv[4], lbraw[RT > 0 ? R / 4 : 1];
+    if (wave < nchunks) {
+        load_x(wave, xv);
+        load_lb(wave, lbraw);
+    }
+
+    for (int c = wave; c < nchunks; c += nwaves) {
+        const int k = c * kChunk + q * 32;
+        const bool more = c + nwaves < nchunks;
+        u32x4 xn[4];
+        if (more) load_x(c + nwaves, xn);
 
         // dense row norm
         float pn = 0.f;
@@ -195,6 +210,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
                 *reinterpret_cast<u32x4*>(lb + lr * 256 + 16 * ((lane & 15) ^ (lr & 15))) =
                     lbraw[j];
             }
+            if (more) load_lb(c + nwaves, lbraw);
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -212,6 +228,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xv[i] = xn[i];
         }
     }
 
