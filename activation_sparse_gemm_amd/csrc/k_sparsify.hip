@@ -8,18 +8,24 @@
 // formed here from the registers that already hold X.
 //
 // Work decomposition (one read of X):
-//   workgroup = 16 rows (tokens) x all of K; waves split K in 128-channel chunks.
-//   lane l: row r = l % 16, quarter q = l / 16; in chunk c it owns channels
-//   [128c + 32q, 128c + 32q + 32): 8 groups of 4, loaded as 4 x 16 bytes.
+//   workgroup = ROWT row tiles of 16 rows (tokens) x all of K; its NW waves
+//   split K in 128-channel chunks.  Lane l: row r = l % 16 of every row tile,
+//   quarter q = l / 16; in chunk c it owns channels [128c + 32q, 128c + 32q + 32)
+//   of each of its ROWT rows: 8 groups of 4 per row, loaded as 4 x 16 bytes.
 //   - selection + packing in registers: 16 kept values (32 B) and 8 codes (4 B)
-//     per lane and chunk, stored in the 16-row x 64-channel tile order of the
-//     packed operand (a workgroup's 16 rows are exactly one tile row-block;
-//     rows past M are written as zero values and codes (0,1));
+//     per row, lane and chunk, stored in the 16-row x 64-channel tile order of
+//     the packed operand (a row tile is exactly one tile row-block; rows past M
+//     in the last existing tile are written as zero values and codes (0,1));
 //   - row norms ||x||^2 and ||x~||^2 with v_dot2_f32_bf16 (products of bf16 are
 //     exact in fp32), summed per chunk in fp32 then in fp64;
 //   - T: the lane's 32 channels are the A operand of 4 v_mfma_f32_16x16x32_bf16
 //     steps (k-block q of each step), LB rows supply the B operand with the same
-//     channel map, one 16-column tile of T per 16 ranks.
+//     channel map, one 16-column tile of T per 16 ranks.  Each LB fragment is
+//     read from the LDS once and used for all ROWT row tiles, so the LB bytes a
+//     workgroup streams from L2 serve 16 ROWT rows.
+//   The launcher takes one row tile per workgroup (8 waves) while one round of
+//   workgroups covers M, else 2 or 3 row tiles (4 waves, to keep the rows'
+//   registers): at M = 9216 three 16-row rounds become one 48-row round.
 //   Partial norms and T are reduced across waves through LDS in a fixed order
 //   (deterministic), then s and bf16 T are written.
 //   Squares of bf16 values are exact in fp32 only while they neither overflow
@@ -37,7 +43,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 16;
 constexpr int kChunk = 128;
-constexpr int kMaxWaves = 8;
 
 // Top-2 of one group of 4 bf16 values given as lo = x0 | x1 << 16 and
 // hi = x2 | x3 << 16.  Returns the 4-bit code i0 | i1 << 2 (i0 < i1) and, in
@@ -89,56 +94,63 @@ __device__ __forceinline__ float dot2_self(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
 
-template <int RT>  // RT = R / 16 column tiles of T (0..4)
-__global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
+// RT = R / 16 column tiles of T (0..4); ROWT row tiles of 16 rows; NW waves
+template <int RT, int ROWT, int NW>
+__global__ __launch_bounds__(NW * 64) void sparsify_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ LB, int M, int K,
     uint16_t* __restrict__ values, uint8_t* __restrict__ meta, float* __restrict__ scale,
     uint16_t* __restrict__ T) {
     constexpr int R = RT * 16;
-    __shared__ double red_norm[kMaxWaves][kRows][2];
-    __shared__ int exact_row[kRows];
+    constexpr int kWgRows = kRows * ROWT;
+    __shared__ double red_norm[NW][kWgRows][2];
+    __shared__ int exact_row[kWgRows];
     // per-wave LB chunk (R rows x 256 B, XOR-swizzled 16-byte pieces); after
     // the main loop the same memory holds the cross-wave T partials
-    constexpr int kLbBytes = RT > 0 ? R * 256 : 64;
-    __shared__ __attribute__((aligned(16))) char lbw[kMaxWaves][kLbBytes];
-    static_assert(sizeof(lbw) >= sizeof(float) * kMaxWaves * kRows * (RT > 0 ? R : 1),
+    constexpr int kLbBytes = RT > 0 ? R * 256 : 64 * ROWT;
+    __shared__ __attribute__((aligned(16))) char lbw[NW][kLbBytes];
+    static_assert(sizeof(lbw) >= sizeof(float) * NW * kWgRows * (RT > 0 ? R : 1),
                   "T partials fit in the LB staging area");
-    float(*red_T)[kRows][RT > 0 ? R : 1] =
-        reinterpret_cast<float(*)[kRows][RT > 0 ? R : 1]>(&lbw[0][0]);
+    float(*red_T)[kWgRows][RT > 0 ? R : 1] =
+        reinterpret_cast<float(*)[kWgRows][RT > 0 ? R : 1]>(&lbw[0][0]);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
     const int r = lane & 15;
     const int q = lane >> 4;
-    const int m0 = blockIdx.x * kRows;
-    const int row = m0 + r;
-    const bool row_ok = row < M;
+    const int m0 = blockIdx.x * kWgRows;
     const int nchunks = K / kChunk;
-
-    const uint16_t* xrow = X + size_t(row_ok ? row : M - 1) * size_t(K);
-    // packed operand, tile order: tile (block b, 64-channel step s) holds 16 rows
-    // x 32 values (1 KB) and 16 rows x 8 meta bytes (128 B)
     const int steps = K / 64;
-    uint16_t* vtile = values + size_t(blockIdx.x) * size_t(steps) * 512 + r * 32;
-    uint8_t* mtile = meta + size_t(blockIdx.x) * size_t(steps) * 128 + r * 8;
 
-    f32x4 acc[RT > 0 ? RT : 1];
+    const uint16_t* xrow[ROWT];
+    bool row_ok[ROWT];
 #pragma unroll
-    for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    double n2 = 0.0, nt2 = 0.0;
+    for (int u = 0; u < ROWT; ++u) {
+        const int row = m0 + 16 * u + r;
+        row_ok[u] = row < M;
+        xrow[u] = X + size_t(row_ok[u] ? row : M - 1) * size_t(K);
+    }
+    // packed operand, tile order: tile (block b, 64-channel step s) holds 16 rows
+    // x 32 values (1 KB) and 16 rows x 8 meta bytes (128 B); row tile u of this
+    // workgroup is block ROWT * blockIdx.x + u
+    uint16_t* vtile = values + size_t(blockIdx.x) * ROWT * size_t(steps) * 512 + r * 32;
+    uint8_t* mtile = meta + size_t(blockIdx.x) * ROWT * size_t(steps) * 128 + r * 8;
 
-    // X: the lane's 32 channels of a chunk.  LB: its rows x the chunk's 128
-    // channels, read as whole row segments (instruction j: rows 4j .. 4j+3,
-    // lane l -> row 4j + l / 16, 16-byte piece l % 16), later put in the
-    // wave's LDS area for the MFMA B operand.  A wave walks its chunks one
-    // after another, so each load is issued a chunk ahead: the next chunk's X
-    // before this chunk is worked on, its LB as soon as this chunk's LB has
-    // gone to the LDS (the same registers).
-    auto load_x = [&](int c, u32x4* xd) {
+    f32x4 acc[ROWT][RT > 0 ? RT : 1];
+#pragma unroll
+    for (int u = 0; u < ROWT; ++u)
+#pragma unroll
+        for (int t = 0; t < (RT > 0 ? RT : 1); ++t) acc[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    double n2[ROWT], nt2[ROWT];
+#pragma unroll
+    for (int u = 0; u < ROWT; ++u) n2[u] = nt2[u] = 0.0;
+
+    auto load_x = [&](int c, u32x4 (*xd)[4]) {
         const int k = c * kChunk + q * 32;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xd[i] = *reinterpret_cast<const u32x4*>(xrow + k + 8 * i);
+        for (int u = 0; u < ROWT; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xd[u][i] = *reinterpret_cast<const u32x4*>(xrow[u] + k + 8 * i);
     };
     auto load_lb = [&](int c, u32x4* ld) {
 #pragma unroll
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
                                                     size_t(c) * kChunk + 8 * (lane & 15));
         }
     };
-    u32x4 xv[4], lbraw[RT > 0 ? R / 4 : 1];
+    u32x4 xv[ROWT][4], lbraw[RT > 0 ? R / 4 : 1];
     if (wave < nchunks) {
         load_x(wave, xv);
         load_lb(wave, lbraw);
@@ -157,43 +169,41 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     for (int c = wave; c < nchunks; c += nwaves) {
         const int k = c * kChunk + q * 32;
         const bool more = c + nwaves < nchunks;
-        u32x4 xn[4];
+        u32x4 xn[ROWT][4];
         if (more) load_x(c + nwaves, xn);
 
-        // dense row norm
-        float pn = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            pn = dot2_self(xv[i].x, pn);
-            pn = dot2_self(xv[i].y, pn);
-            pn = dot2_self(xv[i].z, pn);
-            pn = dot2_self(xv[i].w, pn);
-        }
+        for (int u = 0; u < ROWT; ++u) {
+            float pn = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pn = dot2_self(xv[u][i].x, pn);
+                pn = dot2_self(xv[u][i].y, pn);
+                pn = dot2_self(xv[u][i].z, pn);
+                pn = dot2_self(xv[u][i].w, pn);
+            }
+            uint32_t kept[8];
+            uint32_t code = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                code |= select_group(xv[u][i].x, xv[u][i].y, kept[2 * i]) << (8 * i);
+                code |= select_group(xv[u][i].z, xv[u][i].w, kept[2 * i + 1]) << (8 * i + 4);
+            }
+            float pt = 0.f;
+#pragma unroll
+            for (int g = 0; g < 8; ++g) pt = dot2_self(kept[g], pt);
+            n2[u] += double(pn);
+            nt2[u] += double(pt);
 
-        // selection and packing: group g of this lane is dwords 2g, 2g+1
-        uint32_t kept[8];
-        uint32_t code = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            code |= select_group(xv[i].x, xv[i].y, kept[2 * i]) << (8 * i);
-            code |= select_group(xv[i].z, xv[i].w, kept[2 * i + 1]) << (8 * i + 4);
-        }
-        float pt = 0.f;
-#pragma unroll
-        for (int g = 0; g < 8; ++g) pt = dot2_self(kept[g], pt);
-        n2 += double(pn);
-        nt2 += double(pt);
-
-        {
             // channels k .. k+31 = half (q & 1) of step k / 64
             const int step = k >> 6, half = q & 1;
-            u32x4* vdst = reinterpret_cast<u32x4*>(vtile + step * 512 + half * 16);
-            uint32_t* mdst = reinterpret_cast<uint32_t*>(mtile + step * 128 + half * 4);
-            if (row_ok) {
+            u32x4* vdst = reinterpret_cast<u32x4*>(vtile + (size_t(u) * steps + step) * 512 + half * 16);
+            uint32_t* mdst = reinterpret_cast<uint32_t*>(mtile + (size_t(u) * steps + step) * 128 + half * 4);
+            if (row_ok[u]) {
                 vdst[0] = u32x4{kept[0], kept[1], kept[2], kept[3]};
                 vdst[1] = u32x4{kept[4], kept[5], kept[6], kept[7]};
                 *mdst = code;
-            } else {
+            } else if (m0 + 16 * u < M) {  // padding row of the last (existing) tile
                 vdst[0] = u32x4{0u, 0u, 0u, 0u};
                 vdst[1] = u32x4{0u, 0u, 0u, 0u};
                 *mdst = 0x44444444u;
@@ -201,7 +211,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         }
 
         // T += X LB^T over these channels; B operand of step i: LB row
-        // 16 t + r, channels 32 q + 8 i .. +8 of the chunk
+        // 16 t + r, channels 32 q + 8 i .. +8 of the chunk, read once from the
+        // LDS for all row tiles
         if constexpr (RT > 0) {
             char* lb = lbw[wave];
 #pragma unroll
@@ -220,8 +231,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const bf16x8 bv = *reinterpret_cast<const bf16x8*>(
                         lb + (16 * t + r) * 256 + 16 * ((4 * q + i) ^ r));
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, xv[i]), bv, acc[t], 0, 0, 0);
+#pragma unroll
+                    for (int u = 0; u < ROWT; ++u)
+                        acc[u][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, xv[u][i]), bv, acc[u][t], 0, 0, 0);
                 }
             }
             // the next chunk's writes must not overtake this chunk's reads
@@ -231,29 +244,36 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         }
         if (more) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xv[i] = xn[i];
+            for (int u = 0; u < ROWT; ++u)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xv[u][i] = xn[u][i];
         }
     }
 
     // ---- cross-lane (4 quarters of a row) then cross-wave reductions ----
-    n2 += __shfl_xor(n2, 16);
-    n2 += __shfl_xor(n2, 32);
-    nt2 += __shfl_xor(nt2, 16);
-    nt2 += __shfl_xor(nt2, 32);
-    if (q == 0) {
-        red_norm[wave][r][0] = n2;
-        red_norm[wave][r][1] = nt2;
+#pragma unroll
+    for (int u = 0; u < ROWT; ++u) {
+        double a = n2[u], b = nt2[u];
+        a += __shfl_xor(a, 16);
+        a += __shfl_xor(a, 32);
+        b += __shfl_xor(b, 16);
+        b += __shfl_xor(b, 32);
+        if (q == 0) {
+            red_norm[wave][16 * u + r][0] = a;
+            red_norm[wave][16 * u + r][1] = b;
+        }
     }
     __syncthreads();  // every wave is done with its LB area before it holds T partials
     // accumulator layout of a 16x16 tile: lane (n = l % 16, q) holds rows 4q..4q+3
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
+    for (int u = 0; u < ROWT; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) red_T[wave][4 * q + e][16 * t + r] = acc[t][e];
-    }
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red_T[wave][16 * u + 4 * q + e][16 * t + r] = acc[u][t][e];
     __syncthreads();
 
-    if (threadIdx.x < kRows) {
+    if (threadIdx.x < kWgRows) {
         const int rr = threadIdx.x;
         double a = 0.0, b = 0.0;
         for (int w = 0; w < nwaves; ++w) {
@@ -266,7 +286,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     }
     __syncthreads();
     // exact fp64 pass for rows outside the fast path's range (rare)
-    for (int rr = wave; rr < kRows; rr += nwaves) {
+    for (int rr = wave; rr < kWgRows; rr += nwaves) {
         if (!exact_row[rr]) continue;
         const uint32_t* xr = reinterpret_cast<const uint32_t*>(X + size_t(m0 + rr) * size_t(K));
         double a = 0.0, b = 0.0;
@@ -285,7 +305,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
         if (lane == 0) scale[m0 + rr] = b > 0.0 ? float(sqrt(a / b)) : 1.0f;
     }
     if constexpr (RT > 0) {
-        for (int idx = threadIdx.x; idx < kRows * R; idx += blockDim.x) {
+        for (int idx = threadIdx.x; idx < kWgRows * R; idx += blockDim.x) {
             const int rr = idx / R, cc = idx % R;
             float s = 0.f;
             for (int w = 0; w < nwaves; ++w) s += red_T[w][rr][cc];
@@ -295,34 +315,67 @@ __global__ __launch_bounds__(kMaxWaves * 64) void sparsify_kernel(
     }
 }
 
+// Per-workgroup time of ROWT row tiles (NW = 8 for one tile, 4 for two or
+// three), relative to one tile; measured on the MI355X at K = 3072 and 12288,
+// R = 64 (µs, K = 3072 / 12288: 16.3 / 52.4, 24.0 / 75.0, 29.7 / 92.1).
+constexpr float kRowtCost[4] = {0.f, 1.0f, 1.45f, 1.8f};
+
+template <int RT>
+void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uint16_t* LB,
+               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, hipStream_t stream) {
+    const int nw = rowt == 1 ? 8 : 4;
+    const dim3 grid((M + kRows * rowt - 1) / (kRows * rowt)), block(64 * (nchunks < nw ? nchunks : nw));
+    if (rowt == 1) {
+        hipLaunchKernelGGL((sparsify_kernel<RT, 1, 8>), grid, block, 0, stream, X, LB, M, K, values,
+                           meta, scale, T);
+    } else if (rowt == 2) {
+        hipLaunchKernelGGL((sparsify_kernel<RT, 2, 4>), grid, block, 0, stream, X, LB, M, K, values,
+                           meta, scale, T);
+    } else {
+        hipLaunchKernelGGL((sparsify_kernel<RT, 3, 4>), grid, block, 0, stream, X, LB, M, K, values,
+                           meta, scale, T);
+    }
+}
+
 }  // namespace
 
 lynx_status launch_sparsify(const uint16_t* X, const uint16_t* LB, int M, int K, int R,
                             uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,
                             hipStream_t stream) {
     const int nchunks = K / kChunk;
-    const int nwaves = nchunks < kMaxWaves ? nchunks : kMaxWaves;
-    const dim3 grid((M + kRows - 1) / kRows), block(64 * nwaves);
+    // Row tiles per workgroup: the fewest rounds of workgroups over the compute
+    // units, weighted by the measured cost of a workgroup (one tile when there
+    // is no LoRA: nothing is shared between row tiles then).
+    int rowt = 1;
+    if (R > 0) {
+        int cus = 0;
+        if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
+        const long tiles = (M + kRows - 1) / kRows;
+        float best = 0.f;
+        for (int t = 1; t <= 3; ++t) {
+            const long wgs = (tiles + t - 1) / t;
+            const float c = float((wgs + cus - 1) / cus) * kRowtCost[t];
+            if (t == 1 || c < best) {
+                best = c;
+                rowt = t;
+            }
+        }
+    }
     switch (R / 16) {
         case 0:
-            hipLaunchKernelGGL(sparsify_kernel<0>, grid, block, 0, stream, X, LB, M, K, values,
-                               meta, scale, T);
+            launch_rt<0>(1, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 1:
-            hipLaunchKernelGGL(sparsify_kernel<1>, grid, block, 0, stream, X, LB, M, K, values,
-                               meta, scale, T);
+            launch_rt<1>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 2:
-            hipLaunchKernelGGL(sparsify_kernel<2>, grid, block, 0, stream, X, LB, M, K, values,
-                               meta, scale, T);
+            launch_rt<2>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 3:
-            hipLaunchKernelGGL(sparsify_kernel<3>, grid, block, 0, stream, X, LB, M, K, values,
-                               meta, scale, T);
+            launch_rt<3>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         default:
-            hipLaunchKernelGGL(sparsify_kernel<4>, grid, block, 0, stream, X, LB, M, K, values,
-                               meta, scale, T);
+            launch_rt<4>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
     }
     return launch_status();

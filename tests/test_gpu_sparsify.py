@@ -48,11 +48,13 @@ def test_sparsify_shapes(M, K, R):
     check_sparsify(Xb, LB, f"heavy {M}x{K}")
 
 
-@pytest.mark.parametrize("M,R", [(5000, 64), (4120, 48), (8192, 64)])
+@pytest.mark.parametrize("M,R", [(5000, 64), (4120, 48), (8192, 64), (9000, 64), (12000, 16)])
 def test_sparsify_many_row_blocks(M, R):
-    """More than one round of workgroups on the chip, with ragged and exact M
-    (also guards the packed buffers: a write past them lands in the next
-    output and shows up as a wrong scale)."""
+    """More 16-row tiles than compute units, so workgroups take 2 (M = 4120,
+    5000, 8192) or 3 (M = 9000, 12000) row tiles each, with ragged and exact M:
+    the last workgroup of M = 9000 holds a partial tile and a tile past the
+    padded rows, which it must not write (a write past the packed buffers
+    lands in the next output and shows up as a wrong scale)."""
     Xb = make_activation("heavy", M, 384, seed=M)
     check_sparsify(Xb, make_weights(8, 384, R, seed=R)[2], f"heavy {M}x384")
 
