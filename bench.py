@@ -399,6 +399,11 @@ def main():
                        for L, sk in zip(layers, skipped) if not sk)
     k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
     traffic = traffic_for(K2_SRC, args.workload)
+    # the sparsifier's algorithmic HBM bytes: read X and LB, write the packed
+    # values and meta, s and T (2MK + 2RK + MK + MK/8 + 4M + 2MR per layer)
+    k1_bytes = sum(2 * L.M * L.K + 2 * L.R * L.K + L.M * L.K + L.M * L.K // 8 + 4 * L.M
+                   + 2 * L.M * L.R for L, sk in zip(layers, skipped) if not sk)
+    k1_gbs = k1_bytes / (ms_k1 * 1e-3) / 1e9
     if args.copy_calibration:
         src = torch.ones(COPY_MIB << 19, dtype=torch.bfloat16, device=dev)
         dst = torch.empty_like(src)
@@ -447,6 +452,11 @@ def main():
                      "achieved": round(k2_tflops, 2), "peak": PEAK_DENSE_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(k2_tflops / PEAK_DENSE_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        # the sparsifier against the HBM bound (algorithmic bytes over its
+        # interleaved median time)
+        "sparsify_roofline": {"bound": "hbm", "kernel": "sparsify_kernel (select, norms, pack, LoRA down)",
+                              "achieved": round(k1_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(k1_gbs / PEAK_HBM_GBS, 4), "bytes": k1_bytes},
         # HBM bytes of the profiled K2 launch over its measured time, and the
         # matrix-core busy fractions of the profiled kernels (rocprofv3
         # counters committed under profiles/, null once the kernel changed)
