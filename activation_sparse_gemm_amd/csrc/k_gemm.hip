@@ -223,8 +223,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
 #pragma unroll
         for (int j = 0; j < C::M_DMA; ++j) {
+            // rows 16..31 of each 32-row group (lanes 32..63) land with their
+            // two dwords swapped, so a fragment's 32 rows read 32 banks
             const int blk = 2 * (wave + 4 * j) + (lane >> 5);
-            voffM[j] = (tm0 / 16 + blk) * steps * 128 + 4 * (lane & 31);
+            voffM[j] = (tm0 / 16 + blk) * steps * 128 + 4 * ((lane & 31) ^ (lane >> 5));
         }
     };
     // one of the DMA instructions of a stage (4 value tiles, 2 meta, 2 NB W)
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
                 f.v[x] = lds_read<bf16x8>(As, offA + x * 2048 + 16 * ((2 * sub + h) ^ s64));
                 break;
             case 1:
-                f.i[x] = lds_read<uint16_t>(As + C::A_BYTES, offM + x * 256 + 2 * (2 * sub + h));
+                f.i[x] = lds_read<uint16_t>(As + C::A_BYTES, offM + x * 256 + 2 * (2 * (sub ^ (r >> 4)) + h));
                 break;
             case 2:
                 f.blo[x] = lds_read<bf16x8>(Bs, offB + x * 4096 + 16 * ((4 * sub + h) ^ s128));
