@@ -59,6 +59,14 @@ def test_sparsify_many_row_blocks(M, R):
     check_sparsify(Xb, make_weights(8, 384, R, seed=R)[2], f"heavy {M}x384")
 
 
+@pytest.mark.parametrize("M,K,R", [(9000, 128, 64), (5000, 256, 32), (12000, 128, 16)])
+def test_sparsify_row_tiles_few_waves(M, K, R):
+    """Workgroups of 2 or 3 row tiles whose K has only one or two 128-channel
+    chunks, so they run with fewer waves than rows to reduce."""
+    Xb = make_activation("heavy", M, K, seed=M + K)
+    check_sparsify(Xb, make_weights(8, K, R, seed=R)[2], f"heavy {M}x{K} R{R}")
+
+
 def test_sparsify_gelu_input():
     Xb = make_activation("gelu", 64, 3072, seed=3)
     check_sparsify(Xb, make_weights(8, 3072, 64, seed=3)[2], "gelu 64x3072")
