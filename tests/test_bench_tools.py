@@ -1,0 +1,92 @@
+"""bench.py's counter summaries, on small synthetic profiler databases (CPU).
+
+The HBM-traffic and matrix-core-busy figures that bench.py reports come from
+rocprofv3 results databases turned into committed summaries.  These tests
+feed the summarizers a database with known counter values and check the
+arithmetic: the copy-kernel scale factors, the per-dispatch means, the
+cycles-per-shader-engine division, and that a summary taken on another
+kernel source is ignored.
+"""
+import json
+import os
+import sqlite3
+
+import pytest
+
+import bench
+
+
+def make_db(run_dir, rows):
+    """rows: (kernel_name, counter_name, value), one row per dispatch."""
+    os.makedirs(run_dir, exist_ok=True)
+    con = sqlite3.connect(os.path.join(run_dir, "run_results.db"))
+    con.execute("create table counters_collection (kernel_name text, counter_name text, value real)")
+    con.executemany("insert into counters_collection values (?, ?, ?)", rows)
+    con.commit()
+    con.close()
+
+
+COPY = "void at::native::vectorized_elementwise_kernel<8, at::native::neg_kernel>(int)"
+K2 = "void lynx::(anonymous namespace)::gemm_sparse32<4>(unsigned short const*)"
+K3 = "void lynx::(anonymous namespace)::gemm_dense32<4>(unsigned short const*)"
+
+
+@pytest.fixture
+def root(tmp_path, monkeypatch):
+    os.makedirs(tmp_path / "profiles")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    return tmp_path
+
+
+def test_per_dispatch_mean(tmp_path):
+    make_db(str(tmp_path / "d"), [(K2, "FETCH_SIZE", 10.0), (K2, "FETCH_SIZE", 30.0),
+                                  (K3, "FETCH_SIZE", 7.0), (K2, "WRITE_SIZE", 99.0)])
+    got = bench.per_dispatch_kib(str(tmp_path / "d"), "FETCH_SIZE")
+    assert got == {K2: 20.0, K3: 7.0}
+
+
+def test_traffic_scaled_by_the_copy_kernel(root):
+    # the copy kernel reads and writes COPY_MIB MiB; its counters read half
+    # the fetched bytes and all the written bytes, so the factors are 2 and 1
+    mib = bench.COPY_MIB
+    make_db(str(root / "f"), [(COPY, "FETCH_SIZE", mib * 512.0), (K2, "FETCH_SIZE", 1000.0),
+                              (K2, "FETCH_SIZE", 3000.0)])
+    make_db(str(root / "w"), [(COPY, "WRITE_SIZE", mib * 1024.0), (K2, "WRITE_SIZE", 500.0)])
+    rec = bench.summarize_traffic(str(root / "f"), str(root / "w"), "unit")
+    assert rec["copy_factor_fetch"] == pytest.approx(2.0)
+    assert rec["copy_factor_write"] == pytest.approx(1.0)
+    assert rec["fetch_bytes_per_launch"] == 2000 * 1024 * 2
+    assert rec["write_bytes_per_launch"] == 500 * 1024
+    assert rec["bytes_per_launch"] == 2000 * 1024 * 2 + 500 * 1024
+    saved = json.load(open(root / "profiles" / "traffic_unit.json"))
+    assert saved["kernel_sha"] == bench.source_sha(bench.K2_SRC)
+    # the bench line uses it while the kernel source is unchanged ...
+    assert bench.traffic_for(bench.K2_SRC, "unit") == rec["bytes_per_launch"]
+    # ... and not once it was taken on another source
+    saved["kernel_sha"] = "0" * 16
+    json.dump(saved, open(root / "profiles" / "traffic_unit.json", "w"))
+    assert bench.traffic_for(bench.K2_SRC, "unit") is None
+
+
+def test_traffic_needs_exactly_one_matching_kernel(root):
+    make_db(str(root / "f"), [(K2, "FETCH_SIZE", 1.0)])          # no copy kernel
+    make_db(str(root / "w"), [(COPY, "WRITE_SIZE", 1.0), (K2, "WRITE_SIZE", 1.0)])
+    with pytest.raises(SystemExit):
+        bench.summarize_traffic(str(root / "f"), str(root / "w"), "unit")
+
+
+def test_mfma_busy_fraction(root):
+    # kernel cycles = SQ_BUSY_CYCLES / 32 shader engines; busy = matrix-core
+    # busy cycles over (kernel cycles x 1024 SIMDs)
+    kc = 200000.0
+    make_db(str(root / "s"), [
+        (K2, "SQ_VALU_MFMA_BUSY_CYCLES", 0.5 * kc * 1024), (K2, "SQ_BUSY_CYCLES", kc * 32),
+        (K2, "GRBM_GUI_ACTIVE", 8 * kc),
+        (K3, "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * kc * 1024), (K3, "SQ_BUSY_CYCLES", kc * 32),
+        (COPY, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0), (COPY, "SQ_BUSY_CYCLES", 5.0)])
+    rec = bench.summarize_mfma(str(root / "s"), "unit")
+    assert rec["kernels"]["gemm_sparse32"]["mfma_busy"] == pytest.approx(0.5)
+    assert rec["kernels"]["gemm_sparse32"]["kernel_cycles"] == kc
+    assert rec["kernels"]["gemm_dense32"]["mfma_busy"] == pytest.approx(0.25)
+    assert not any("neg" in k for k in rec["kernels"])           # no matrix work: left out
+    assert bench.mfma_busy_for(bench.K2_SRC, "unit") == {"gemm_sparse32": 0.5, "gemm_dense32": 0.25}
