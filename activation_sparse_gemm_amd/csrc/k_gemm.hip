@@ -148,6 +148,46 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Stores one wave's 128 x 32 NB output block straight from the accumulators,
+// for tiles whose columns all lie inside N (N % 8 == 0).  A lane holds one
+// column of each 32 x 32 tile, rows 8 (e / 4) + 4 h + e % 4.  Rows e and e + 1
+// (e even) are converted together; the pair is swapped with the neighbouring
+// column's lane (DPP quad permute) and each lane keeps one row of both
+// columns: even columns row e, odd columns row e + 1.  Each store writes two
+// adjacent outputs, and a half-wave's 16 lanes cover 64 contiguous bytes of a
+// row.  Rows past M lie past the end of the buffer resource and are dropped.
+// row0, col0: the block's first output row and column.
+template <int NB>
+__device__ __forceinline__ void store_block_direct(const f32x16 (&acc)[4][NB],
+                                                   __amdgpu_buffer_rsrc_t rsY, int N, int row0,
+                                                   int col0) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const int el = fresh_lane();
+    const int er = el & 31, eh = el >> 5;
+    // v_perm_b32 selectors over {partner pair : own pair}: even columns take
+    // the low halves (row e of own and partner column), odd the high halves
+    const uint32_t psel = (er & 1) ? 0x03020706u : 0x05040100u;
+    const uint32_t vbase =
+        (uint32_t(row0 + 4 * eh + (er & 1)) * uint32_t(N) + uint32_t(col0 + (er & ~1))) * 2u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                const uint32_t own = __builtin_bit_cast(
+                    uint32_t,
+                    __builtin_convertvector(f32x2_t{acc[a][b][e], acc[a][b][e + 1]}, bf16x2_t));
+                const uint32_t partner =
+                    uint32_t(__builtin_amdgcn_update_dpp(0, int(own), 0xB1, 0xF, 0xF, false));
+                const uint32_t w = __builtin_amdgcn_perm(partner, own, psel);
+                const uint32_t soff =
+                    (uint32_t(32 * a + 8 * (e / 4) + (e % 4)) * uint32_t(N) + uint32_t(32 * b)) * 2u;
+                __builtin_amdgcn_raw_buffer_store_b32(w, rsY, vbase, soff, 0);
+            }
+}
+
 // ---------------------------------------------------------------------------
 // K2: Y = s * (X~ W^T) + T LA^T with v_smfmac_f32_32x32x32_bf16.
 //
@@ -563,56 +603,62 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
             }
         }
 
-        // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
-        // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
-        // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
-        // Staging rows 4..7 have their 128-byte halves swapped so the two
-        // halves of the wave write different banks.
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int lr = 4 * h + i;  // staging row 0..7
-                        *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
-                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
-                    }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
-                // (of the wave's WC columns)
-                const int el = fresh_lane();
-                const int srow = el >> 3;
-                const int orow = m0 + rbase + srow;
-                const int ocol = n0 + wn * WC + (el & 7) * 16;
-                if (orow < M && (el & 7) < 2 * NB) {
-                    const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
-                        const int col = ocol + 8 * i;
-                        const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
-                        if (vec_ok && col + 8 <= N) {
-                            __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
-                        } else {
-                            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                            for (int q2 = 0; q2 < 8; ++q2)
-                                if (col + q2 < N)
-                                    __builtin_amdgcn_raw_buffer_store_b16(
-                                        uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
-                                        yoff + 2u * q2, 0, 0);
+        // ---- epilogue: interior tiles straight from the accumulators, edge
+        // tiles (columns past N, or N % 8 != 0) through the LDS staging rows
+        if (vec_ok && n0 + TN <= N) {
+            store_block_direct<NB>(acc, rsY, N, m0 + wm * 128, n0 + wn * WC);
+        } else {
+            // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
+            // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
+            // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
+            // Staging rows 4..7 have their 128-byte halves swapped so the two
+            // halves of the wave write different banks.
+    #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
+    #pragma unroll
+                    for (int b = 0; b < NB; ++b)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int lr = 4 * h + i;  // staging row 0..7
+                            *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
+                                __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
+                        }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
+                    // (of the wave's WC columns)
+                    const int el = fresh_lane();
+                    const int srow = el >> 3;
+                    const int orow = m0 + rbase + srow;
+                    const int ocol = n0 + wn * WC + (el & 7) * 16;
+                    if (orow < M && (el & 7) < 2 * NB) {
+                        const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
+    #pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
+                            const int col = ocol + 8 * i;
+                            const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
+                            if (vec_ok && col + 8 <= N) {
+                                __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
+                            } else {
+                                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    #pragma unroll
+                                for (int q2 = 0; q2 < 8; ++q2)
+                                    if (col + q2 < N)
+                                        __builtin_amdgcn_raw_buffer_store_b16(
+                                            uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
+                                            yoff + 2u * q2, 0, 0);
+                            }
                         }
                     }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
         __syncthreads();  // T / LA slots, s and the staging rows are free
@@ -837,51 +883,56 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
         for (int t = nk - 4; t < nk; ++t)
             stage(t, std::false_type{}, (t + 2 < nk ? kDma : nx) + (t + 3 < nk ? kDma : nx));
 
-        // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
-        // (the same staging as K2's epilogue, scale 1)
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int rbase = wm * 128 + 32 * a + 8 * j;
-#pragma unroll
-                for (int b = 0; b < NB; ++b)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int lr = 4 * h + i;
-                        *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
-                            __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
-                    }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const int el = fresh_lane();
-                const int srow = el >> 3;
-                const int orow = m0 + rbase + srow;
-                const int ocol = n0 + wn * WC + (el & 7) * 16;
-                if (orow < M && (el & 7) < 2 * NB) {
-                    const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
-#pragma unroll
-                    for (int i = 0; i < 2; ++i) {
-                        const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
-                        const int col = ocol + 8 * i;
-                        const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
-                        if (vec_ok && col + 8 <= N) {
-                            __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
-                        } else {
-                            const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                            for (int q2 = 0; q2 < 8; ++q2)
-                                if (col + q2 < N)
-                                    __builtin_amdgcn_raw_buffer_store_b16(
-                                        uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
-                                        yoff + 2u * q2, 0, 0);
+        // ---- epilogue: as in K2 (interior tiles direct, edge tiles staged)
+        if (vec_ok && n0 + TN <= N) {
+            store_block_direct<NB>(acc, rsY, N, m0 + wm * 128, n0 + wn * WC);
+        } else {
+            // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
+            // (the same staging as K2's epilogue, scale 1)
+    #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rbase = wm * 128 + 32 * a + 8 * j;
+    #pragma unroll
+                    for (int b = 0; b < NB; ++b)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int lr = 4 * h + i;
+                            *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
+                                __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
+                        }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    const int el = fresh_lane();
+                    const int srow = el >> 3;
+                    const int orow = m0 + rbase + srow;
+                    const int ocol = n0 + wn * WC + (el & 7) * 16;
+                    if (orow < M && (el & 7) < 2 * NB) {
+                        const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
+    #pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
+                            const int col = ocol + 8 * i;
+                            const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
+                            if (vec_ok && col + 8 <= N) {
+                                __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
+                            } else {
+                                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    #pragma unroll
+                                for (int q2 = 0; q2 < 8; ++q2)
+                                    if (col + q2 < N)
+                                        __builtin_amdgcn_raw_buffer_store_b16(
+                                            uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
+                                            yoff + 2u * q2, 0, 0);
+                            }
                         }
                     }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
         // the next tile's stages 0..2 and half of 3 are in sl[0..3]
