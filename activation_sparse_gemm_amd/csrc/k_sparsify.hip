@@ -284,7 +284,20 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
         exact_row[rr] = (m0 + rr < M) && !safe;
         if (m0 + rr < M && safe) scale[m0 + rr] = float(sqrt(a / b));
     }
-    __syncthreads();
+    // T = the waves' partials summed in wave order, four columns per thread
+    // (it does not wait for the exact-row decisions above)
+    if constexpr (RT > 0) {
+        typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+        for (int idx = threadIdx.x; idx < kWgRows * R / 4; idx += blockDim.x) {
+            const int rr = idx / (R / 4), c4 = 4 * (idx % (R / 4));
+            f32x4 sm = *reinterpret_cast<const f32x4*>(&red_T[0][rr][c4]);
+            for (int w = 1; w < nwaves; ++w) sm += *reinterpret_cast<const f32x4*>(&red_T[w][rr][c4]);
+            if (m0 + rr < M)
+                *reinterpret_cast<u32x2*>(T + size_t(m0 + rr) * R + c4) =
+                    __builtin_bit_cast(u32x2, __builtin_convertvector(sm, bf16x4_t));
+        }
+    }
+    __syncthreads();  // exact_row is complete
     // exact fp64 pass for rows outside the fast path's range (rare)
     for (int rr = wave; rr < kWgRows; rr += nwaves) {
         if (!exact_row[rr]) continue;
@@ -303,15 +316,6 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
         a = wave_sum(a);
         b = wave_sum(b);
         if (lane == 0) scale[m0 + rr] = b > 0.0 ? float(sqrt(a / b)) : 1.0f;
-    }
-    if constexpr (RT > 0) {
-        for (int idx = threadIdx.x; idx < kWgRows * R; idx += blockDim.x) {
-            const int rr = idx / R, cc = idx % R;
-            float s = 0.f;
-            for (int w = 0; w < nwaves; ++w) s += red_T[w][rr][cc];
-            if (m0 + rr < M)
-                T[size_t(m0 + rr) * R + cc] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(s));
-        }
     }
 }
 
