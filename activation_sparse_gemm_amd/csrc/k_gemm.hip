@@ -43,7 +43,7 @@ namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 256, BN = 256, NT = 256, GROUP_M = 8;
+constexpr int BM = 256, NT = 256, GROUP_M = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit format
 
 // K2's stage: 64 dense channels of a 256 x (64 NB) tile (NB = 4 or 3 column
@@ -93,14 +93,16 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 
 // One wave-wide global -> LDS copy: lane l's 16 (or 4) bytes at
 // rsrc + voff + soff land at LDS byte lds + 16 l (or 4 l).  The buffer range
-// check covers voff only, so voff carries the row and soff the k offset.
-__device__ __forceinline__ void dma16(uint32_t lds, int voff, i32x4 rsrc, int soff) {
+// check covers voff only, so voff carries the row and soff the k offset (a
+// row inside the buffer stays inside it at every k).  Offsets are unsigned
+// 32-bit byte offsets; the shape limits keep every padded row below 2^32.
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
                  : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(uint32_t lds, int voff, i32x4 rsrc, int soff) {
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                  :
                  : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
@@ -155,7 +157,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // column's lane (DPP quad permute) and each lane keeps one row of both
 // columns: even columns row e, odd columns row e + 1.  Each store writes two
 // adjacent outputs, and a half-wave's 16 lanes cover 64 contiguous bytes of a
-// row.  Rows past M lie past the end of the buffer resource and are dropped.
+// row.  The whole byte offset, row part included, goes in the VGPR offset,
+// which the buffer range check covers (the SGPR offset is not checked): rows
+// past M lie past the end of the buffer resource and are dropped.  The shape
+// limits keep (M + 256) N < 2^31, so the offsets of those rows cannot wrap.
 // row0, col0: the block's first output row and column.
 template <int NB>
 __device__ __forceinline__ void store_block_direct(const f32x16 (&acc)[4][NB],
@@ -182,9 +187,9 @@ __device__ __forceinline__ void store_block_direct(const f32x16 (&acc)[4][NB],
                 const uint32_t partner =
                     uint32_t(__builtin_amdgcn_update_dpp(0, int(own), 0xB1, 0xF, 0xF, false));
                 const uint32_t w = __builtin_amdgcn_perm(partner, own, psel);
-                const uint32_t soff =
+                const uint32_t roff =
                     (uint32_t(32 * a + 8 * (e / 4) + (e % 4)) * uint32_t(N) + uint32_t(32 * b)) * 2u;
-                __builtin_amdgcn_raw_buffer_store_b32(w, rsY, vbase, soff, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(w, rsY, vbase + roff, 0, 0);
             }
 }
 
@@ -249,37 +254,37 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const i32x4 rsT = make_rsrc(T, uint32_t(M) * uint32_t(2 * R));
     const i32x4 rsL = make_rsrc(LA, uint32_t(N) * uint32_t(2 * R));
     const i32x4 rsS = make_rsrc(scale, uint32_t(M) * 4u);
-    int voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA];
+    uint32_t voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA];
     auto set_tile_offsets = [&](int tm0, int tn0) {
 #pragma unroll
         for (int j = 0; j < C::A_DMA; ++j) {
             const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
-            voffA[j] = (tm0 / 16 + blk) * steps * 1024 + row * 64 + 16 * (ph ^ swz64(row));
+            voffA[j] = uint32_t(tm0 / 16 + blk) * uint32_t(steps) * 1024u + uint32_t(row * 64 + 16 * (ph ^ swz64(row)));
         }
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
             const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
-            voffB[j] = (tn0 + row) * 2 * K + 16 * (ph ^ swz128(row));
+            voffB[j] = uint32_t(tn0 + row) * uint32_t(2 * K) + uint32_t(16 * (ph ^ swz128(row)));
         }
 #pragma unroll
         for (int j = 0; j < C::M_DMA; ++j) {
             // rows 16..31 of each 32-row group (lanes 32..63) land with their
             // two dwords swapped, so a fragment's 32 rows read 32 banks
             const int blk = 2 * (wave + 4 * j) + (lane >> 5);
-            voffM[j] = (tm0 / 16 + blk) * steps * 128 + 4 * ((lane & 31) ^ (lane >> 5));
+            voffM[j] = uint32_t(tm0 / 16 + blk) * uint32_t(steps) * 128u + uint32_t(4 * ((lane & 31) ^ (lane >> 5)));
         }
     };
     // one of the DMA instructions of a stage (4 value tiles, 2 meta, 2 NB W)
     auto dma_k = [&](int t, uint32_t slot_off, int k) {
         const uint32_t base = lds0 + slot_off;
         if (k < C::A_DMA) {
-            dma16(base + 1024 * (wave + 4 * k), voffA[k], rsA, t * 1024);
+            dma16(base + 1024 * (wave + 4 * k), voffA[k], rsA, uint32_t(t) * 1024u);
         } else if (k < C::A_DMA + C::M_DMA) {
             const int j = k - C::A_DMA;
-            dma4(base + C::A_BYTES + 256 * (wave + 4 * j), voffM[j], rsM, t * 128);
+            dma4(base + C::A_BYTES + 256 * (wave + 4 * j), voffM[j], rsM, uint32_t(t) * 128u);
         } else {
             const int j = k - C::A_DMA - C::M_DMA;
-            dma16(base + C::A_BYTES + C::META_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB, t * 128);
+            dma16(base + C::A_BYTES + C::META_BYTES + 1024 * (wave + 4 * j), voffB[j], rsB, uint32_t(t) * 128u);
         }
     };
 
@@ -381,12 +386,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         const int row = 8 * (wave + 4 * j) + (lane >> 3);
         const int c = (lane & 7) ^ swz128(row);
         const int base = is_T ? m0 : n0;
-        const int voff = 8 * c < R ? (base + row) * 2 * R + 16 * c : 0x7FFFFFF0;
+        const uint32_t voff = 8 * c < R ? uint32_t(base + row) * uint32_t(2 * R) + uint32_t(16 * c) : 0xFFFFFFF0u;
         dma16(lds0 + uint32_t(soff) + 1024 * (wave + 4 * j), voff, is_T ? rsT : rsL, 0);
     };
     // wave w's quarter of the tile's s: rows 64 w + l
     auto dma_scale = [&]() {
-        dma4(lds0 + C::SCALE_OFF + 256 * wave, (m0 + 64 * wave + lane) * 4, rsS, 0);
+        dma4(lds0 + C::SCALE_OFF + 256 * wave, uint32_t(m0 + 64 * wave + lane) * 4u, rsS, 0);
     };
     bool has_next = false;
     // instruction i (0..kHalf-1) of half `half` of a stage of kind KIND; the
@@ -727,28 +732,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
         reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)smem));
     const i32x4 rsA = make_rsrc(X, uint32_t(M) * uint32_t(2 * K));
     const i32x4 rsB = make_rsrc(W, uint32_t(N) * uint32_t(2 * K));
-    int voffA[kDmaA], voffB[kDmaB];      // current tile
-    auto offsets = [&](int tm0, int tn0, int* oa, int* ob) {
+    uint32_t voffA[kDmaA], voffB[kDmaB];  // current tile
+    auto offsets = [&](int tm0, int tn0, uint32_t* oa, uint32_t* ob) {
         const int l = fresh_lane();
 #pragma unroll
         for (int j = 0; j < kDmaA; ++j) {
             const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
-            oa[j] = (tm0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+            oa[j] = uint32_t(tm0 + row) * uint32_t(2 * K) + uint32_t(16 * (ph ^ swz64(row)));
         }
 #pragma unroll
         for (int j = 0; j < kDmaB; ++j) {
             const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
-            ob[j] = (tn0 + row) * 2 * K + 16 * (ph ^ swz64(row));
+            ob[j] = uint32_t(tn0 + row) * uint32_t(2 * K) + uint32_t(16 * (ph ^ swz64(row)));
         }
     };
     // DMA instruction k (0..7) of stage t (of the tile whose offsets are oa/ob)
-    auto dma = [&](const int* oa, const int* ob, int t, int soff, int k) {
+    auto dma = [&](const uint32_t* oa, const uint32_t* ob, int t, int soff, int k) {
         const uint32_t base = lds0 + uint32_t(soff);
         if (k < kDmaA) {
-            dma16(base + 1024 * (wave + 4 * k), oa[k], rsA, t * kRow);
+            dma16(base + 1024 * (wave + 4 * k), oa[k], rsA, uint32_t(t * kRow));
         } else {
             const int j = k - kDmaA;
-            dma16(base + kABytes + 1024 * (wave + 4 * j), ob[j], rsB, t * kRow);
+            dma16(base + kABytes + 1024 * (wave + 4 * j), ob[j], rsB, uint32_t(t * kRow));
         }
     };
 
@@ -792,9 +797,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
             const int j = k < kDmaA ? k : k - kDmaA;
             const int l = fresh_lane();
             const int row = 16 * (wave + 4 * j) + (l >> 2), ph = l & 3;
-            const int off = ((k < kDmaA ? m0n : n0n) + row) * 2 * K + 16 * (ph ^ swz64(row));
+            const uint32_t off = uint32_t((k < kDmaA ? m0n : n0n) + row) * uint32_t(2 * K) +
+                                 uint32_t(16 * (ph ^ swz64(row)));
             dma16(lds0 + uint32_t(soff) + (k < kDmaA ? 0 : kABytes) + 1024 * (wave + 4 * j), off,
-                  k < kDmaA ? rsA : rsB, (u - nk) * kRow);
+                  k < kDmaA ? rsA : rsB, uint32_t((u - nk) * kRow));
         }
     };
 

@@ -15,6 +15,12 @@ std::atomic<int> g_cu_count[kMaxDevices];    // 0 unknown
 
 constexpr int64_t kMaxDim = int64_t(1) << 24;
 constexpr int64_t kMaxElems = int64_t(1) << 31;
+// The tiled GEMMs address every operand with unsigned 32-bit byte offsets
+// through buffer resources, including the rows and columns of a last partial
+// 256-wide tile that lie past the tensor (the range check drops them); with
+// the dimensions padded by one tile the tensors stay below 2^31 elements, so
+// those offsets stay below 2^32 and never wrap into the tensor.
+constexpr int64_t kPad = 256;
 
 inline size_t round_up256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -24,7 +30,8 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0) return false;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
     if (K % 128 != 0) return false;
-    if (M * K >= kMaxElems || N * K >= kMaxElems || M * N >= kMaxElems) return false;
+    if ((M + kPad) * K >= kMaxElems || (N + kPad) * K >= kMaxElems || (M + kPad) * N >= kMaxElems)
+        return false;
     return true;
 }
 
@@ -83,6 +90,45 @@ lynx_status device_cu_count(int* cus) {
     return LYNX_OK;
 }
 
+}  // namespace lynx
+
+namespace lynx {
+lynx_status validate_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                                  const uint16_t* LB, const uint16_t* Y, int64_t M, int64_t N,
+                                  int64_t K, int64_t R, bool* noop) {
+    *noop = false;
+    if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
+    if (M == 0 || N == 0) {
+        *noop = true;
+        return LYNX_OK;
+    }
+    if (!X || !W || !Y) return LYNX_ERR_NULL;
+    if (R > 0 && (!LA || !LB)) return LYNX_ERR_NULL;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
+    if (R > 0 && (!aligned16(LA) || !aligned16(LB))) return LYNX_ERR_ALIGN;
+    return LYNX_OK;
+}
+
+size_t sparse_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+    return layout_for(M, K, R).total;
+}
+
+// the sparse layer on validated arguments
+lynx_status run_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                             const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                             int64_t R, void* workspace, hipStream_t s) {
+    const WorkspaceLayout L = layout_for(M, K, R);
+    char* ws = static_cast<char*>(workspace);
+    uint16_t* values = reinterpret_cast<uint16_t*>(ws + L.values);
+    uint8_t* meta = reinterpret_cast<uint8_t*>(ws + L.meta);
+    float* scale = reinterpret_cast<float*>(ws + L.scale);
+    uint16_t* T = R > 0 ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
+    lynx_status st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values,
+                                     meta, scale, T, s);
+    if (st != LYNX_OK) return st;
+    return launch_gemm_sparse(values, meta, scale, T, W, R > 0 ? LA : nullptr, Y, int(M), int(N),
+                              int(K), int(R), s);
+}
 }  // namespace lynx
 
 using namespace lynx;
@@ -146,22 +192,16 @@ lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t
                               static_cast<hipStream_t>(stream));
 }
 
+
 namespace {
-// Argument checks of the sparse layer; LYNX_OK with *noop set for M or N == 0.
+// Argument checks of the sparse layer with a caller workspace; LYNX_OK with
+// *noop set for M or N == 0.
 lynx_status validate_sparse(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
                             const uint16_t* LB, const uint16_t* Y, int64_t M, int64_t N,
                             int64_t K, int64_t R, const void* workspace, size_t workspace_bytes,
                             bool* noop) {
-    *noop = false;
-    if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
-    if (M == 0 || N == 0) {
-        *noop = true;
-        return LYNX_OK;
-    }
-    if (!X || !W || !Y) return LYNX_ERR_NULL;
-    if (R > 0 && (!LA || !LB)) return LYNX_ERR_NULL;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
-    if (R > 0 && (!aligned16(LA) || !aligned16(LB))) return LYNX_ERR_ALIGN;
+    lynx_status st = validate_sparse_layer(X, W, LA, LB, Y, M, N, K, R, noop);
+    if (st != LYNX_OK || *noop) return st;
     if (!workspace || workspace_bytes < layout_for(M, K, R).total) return LYNX_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LYNX_ERR_ALIGN;
     return LYNX_OK;
@@ -179,23 +219,6 @@ lynx_status validate_dense(const uint16_t* X, const uint16_t* W, const uint16_t*
     if (!aligned16(X) || !aligned16(W) || !aligned16(Y)) return LYNX_ERR_ALIGN;
     return LYNX_OK;
 }
-
-// the sparse layer on validated arguments
-lynx_status run_sparse(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
-                       const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K, int64_t R,
-                       void* workspace, hipStream_t s) {
-    const WorkspaceLayout L = layout_for(M, K, R);
-    char* ws = static_cast<char*>(workspace);
-    uint16_t* values = reinterpret_cast<uint16_t*>(ws + L.values);
-    uint8_t* meta = reinterpret_cast<uint8_t*>(ws + L.meta);
-    float* scale = reinterpret_cast<float*>(ws + L.scale);
-    uint16_t* T = R > 0 ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
-    lynx_status st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values,
-                                     meta, scale, T, s);
-    if (st != LYNX_OK) return st;
-    return launch_gemm_sparse(values, meta, scale, T, W, R > 0 ? LA : nullptr, Y, int(M), int(N),
-                              int(K), int(R), s);
-}
 }  // namespace
 
 lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
@@ -208,7 +231,8 @@ lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const 
     if (st != LYNX_OK || noop) return st;
     st = check_device();
     if (st != LYNX_OK) return st;
-    return run_sparse(X, W, LA, LB, Y, M, N, K, R, workspace, static_cast<hipStream_t>(stream));
+    return run_sparse_layer(X, W, LA, LB, Y, M, N, K, R, workspace,
+                            static_cast<hipStream_t>(stream));
 }
 
 lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
@@ -272,7 +296,7 @@ lynx_status lynx_linear_sequence(const lynx_layer* layers, int64_t n, void* work
         if (L.mode == LYNX_LAYER_DENSE) {
             st = launch_gemm_dense(L.X, L.W, L.Y, int(L.M), int(L.N), int(L.K), s);
         } else {
-            st = run_sparse(L.X, L.W, L.LA, L.LB, L.Y, L.M, L.N, L.K, L.R, workspace, s);
+            st = run_sparse_layer(L.X, L.W, L.LA, L.LB, L.Y, L.M, L.N, L.K, L.R, workspace, s);
         }
         if (st != LYNX_OK) return st;
     }

@@ -28,6 +28,23 @@ inline lynx_status launch_status() {
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// ---- the sparse layer, shared by the entry points -------------------------
+// Argument checks of the sparse + LoRA layer (everything but its workspace);
+// LYNX_OK with *noop set when M or N is 0.
+lynx_status validate_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                                  const uint16_t* LB, const uint16_t* Y, int64_t M, int64_t N,
+                                  int64_t K, int64_t R, bool* noop);
+
+// Workspace bytes of the sparse layer (valid sizes only).
+size_t sparse_workspace_bytes(int64_t M, int64_t K, int64_t R);
+
+// The sparsifier then the sparse GEMM, on validated arguments, with the
+// packed operand, s and T in `workspace` (sparse_workspace_bytes, 256-byte
+// aligned).
+lynx_status run_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
+                             const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K,
+                             int64_t R, void* workspace, hipStream_t s);
+
 // ---- kernel launchers (validated arguments only) ---------------------------
 lynx_status launch_sparsify(const uint16_t* X, const uint16_t* LB, int M, int K, int R,
                             uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,

@@ -32,7 +32,9 @@
  *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs.
  *   - Shape limits: K is a positive multiple of 128; M >= 0 and N >= 0 (0 is a
  *     no-op); R (LoRA rank) is one of 0, 16, 32, 48, 64 (0 = no LoRA branch);
- *     M, N, K <= 2^24 and every tensor smaller than 2^31 elements.
+ *     M, N, K <= 2^24; (M + 256) * K, (N + 256) * K and (M + 256) * N are each
+ *     below 2^31 (every tensor, padded by one 256-row tile, smaller than 2^31
+ *     elements, so that 32-bit byte offsets cover it).
  *   - The current device must be gfx950 (MI350 series); otherwise
  *     LYNX_ERR_UNSUPPORTED_DEVICE.
  *

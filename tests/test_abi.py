@@ -116,6 +116,45 @@ def test_dense_validation(args, status):
     assert _abi.lib().lynx_linear_dense(*args, None) == status
 
 
+# The tiled kernels address every operand with unsigned 32-bit byte offsets,
+# padded rows and columns of a partial 256-wide tile included: (M + 256) K,
+# (N + 256) K and (M + 256) N must each stay below 2^31 elements.
+LIMIT = 1 << 31
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (LIMIT // 16384 - 256, 16, 16384),      # (M + 256) K == 2^31
+    (16, LIMIT // 16384 - 256, 16384),      # (N + 256) K == 2^31
+    ((1 << 20) - 256, 2048, 128),           # (M + 256) N == 2^31
+])
+def test_shape_limit_of_32bit_offsets_rejects(M, N, K):
+    lib = _abi.lib()
+    assert call_linear(M=M, N=N, K=K) == SHAPE
+    assert call_packed(M=M, N=N, K=K) == SHAPE
+    assert lib.lynx_linear_dense(A, A, A, M, N, K, None) == SHAPE
+    assert call_sequence(layers_of((M, N, K, 16, SP))) == SHAPE
+    if (M + 256) * K >= LIMIT:
+        assert call_sparsify(M=M, K=K) == SHAPE
+        assert _abi.workspace_bytes(M, K, 16) == 0
+
+
+@pytest.mark.parametrize("M,N,K", [
+    (LIMIT // 16384 - 257, 16, 16384), (16, LIMIT // 16384 - 257, 16384),
+    ((1 << 20) - 256, 2047, 128),
+])
+def test_shape_limit_of_32bit_offsets_admits(M, N, K):
+    """One row or column below the limit passes validation: without a GPU the
+    call stops at the device check (it never launches)."""
+    import torch
+    assert _abi.workspace_bytes(M, K, 16) > 0
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
+    assert call_linear(M=M, N=N, K=K, wsb=1 << 40) == UNSUPPORTED
+    assert call_packed(M=M, N=N, K=K) == UNSUPPORTED
+    assert _abi.lib().lynx_linear_dense(A, A, A, M, N, K, None) == UNSUPPORTED
+    assert call_sparsify(M=M, K=K) == UNSUPPORTED
+
+
 def test_probe_validation():
     L = _abi.lib()
     assert L.lynx_probe_mfma(4, 0, A, A, A, A, None) == SHAPE

@@ -137,3 +137,80 @@ def test_sparsify_full_size(M, K, kind):
     rows = np.unique(np.concatenate([np.arange(0, M, 97), [M - 1]]))
     T_ref = orc.decode_bf16(Xb[rows]) @ orc.decode_bf16(LB).T
     assert row_rel_err(host_f64(T)[rows], T_ref).max() <= ROW_REL_TOL
+
+
+def extreme_row(kind, K, rng):
+    """One row whose squares leave fp32's range (or vanish), so its norm
+    takes the exact fp64 pass."""
+    sign = np.where(rng.random(K) < 0.5, 0x8000, 0).astype(np.uint16)
+    if kind == "max":          # the largest finite bf16: squares overflow fp32
+        return (0x7F7F | sign).astype(np.uint16)
+    if kind == "huge":         # |x| in [2^70, 2^71): squares overflow fp32
+        return (0x6280 + rng.integers(0, 128, K) | sign).astype(np.uint16)
+    if kind == "subnormal":    # squares underflow to zero in fp32
+        return (rng.integers(1, 128, K) | sign).astype(np.uint16)
+    if kind == "tiny":         # 2^-70 .. : squares below 2^-60 in sum
+        return (0x1C80 + rng.integers(0, 128, K) | sign).astype(np.uint16)
+    if kind == "zero":
+        return np.zeros(K, dtype=np.uint16)
+    if kind == "mixed":        # smallest normals next to subnormals
+        r = (rng.integers(1, 128, K) | sign).astype(np.uint16)
+        r[::3] = 0x0080 | sign[::3]
+        return r
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("M", [5000, 9000])
+def test_sparsify_extreme_rows_across_row_tiles(M):
+    """Rows that take the exact fp64 norm pass, scattered over row tiles and
+    workgroups when a workgroup holds 2 (M = 5000) or 3 (M = 9000) row tiles,
+    with the rank-64 LoRA: packed operand bit-exact, s within 1e-5 (and,
+    on the exact rows, the fp64 value rounded once to fp32), T on the rows
+    whose products stay in range."""
+    K, R = 384, 64
+    rng = np.random.default_rng(M)
+    Xb = make_activation("heavy", M, K, seed=M + 1)
+    LB = make_weights(8, K, R, seed=3)[2]
+    tiles = (M + 15) // 16
+    kinds = ["max", "huge", "subnormal", "tiny", "zero", "mixed"]
+    special = {}
+    for t in sorted({0, 1, 2, 3, 5, tiles // 3, tiles // 2, tiles - 3, tiles - 2, tiles - 1}):
+        for j, r in enumerate((0, 5, 15) if t % 2 == 0 else (3, 8, 12)):
+            m = 16 * t + r
+            if m < M:
+                k = kinds[(t + j) % len(kinds)]
+                Xb[m] = extreme_row(k, K, rng)
+                special[m] = k
+    rows = np.array(sorted(special))
+    say(f"sparsify extreme rows M={M} K={K} R={R}: {len(rows)} special rows")
+    values, meta, scale, T = lynx.sparsify(dev(Xb), dev(LB))
+    torch.cuda.synchronize()
+    ref = orc.sparsify(Xb, LB)
+    np.testing.assert_array_equal(meta.cpu().numpy(), ref.meta_stored(), err_msg="meta")
+    np.testing.assert_array_equal(host_bits(values), ref.values_stored(), err_msg="values")
+    s = scale.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(s / ref.scale - 1)) <= SCALE_REL_TOL, "scale"
+    assert np.max(np.abs(s[rows] / ref.scale[rows] - 1)) <= 2.0 ** -23, "scale of exact rows"
+    assert np.all(s[[m for m in rows if special[m] == "zero"]] == 1.0)
+    # T: rows of the largest finite value overflow fp32 and bf16 (outside the
+    # contract's range); every other row within 5e-3
+    ok = np.array([special.get(m) != "max" for m in range(M)])
+    Tg = host_f64(T)
+    rep = report(f"extreme rows M={M} T", Tg[ok], ref.T[ok])
+    assert rep["max_row_rel"] <= ROW_REL_TOL and rep["nonfinite"] == 0
+    assert np.all(Tg[[m for m in rows if special[m] == "zero"]] == 0)
+
+
+def test_sparsify_is_deterministic_three_row_tiles():
+    """Workgroups of three row tiles (M = 9000, R = 64): two calls give the
+    same bits in every output."""
+    Xb = make_activation("heavy", 9000, 3072, seed=9)
+    LB = make_weights(8, 3072, 64, seed=9)[2]
+    X, L = dev(Xb), dev(LB)
+    say("sparsify determinism M=9000 K=3072 R=64 (3 row tiles per workgroup)")
+    a = [t.clone() for t in lynx.sparsify(X, L)]
+    b = lynx.sparsify(X, L)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
+                           y.view(torch.uint8) if y.dtype != torch.uint8 else y)

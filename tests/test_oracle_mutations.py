@@ -20,6 +20,7 @@ PIN_TESTS = [
     lambda: pins.test_all_plus_minus_one_closed_form(),
     lambda: pins.test_tiny_layer_brute_force(4, 32, 5, 3, 0),
     lambda: pins.test_tiny_layer_brute_force(3, 16, 8, 2, 1),
+    lambda: pins.test_packed_path_with_lora_brute_force(),
 ]
 
 
@@ -105,8 +106,30 @@ def _layer_lora_la_lb_swapped_roles(X_bits, W_bits, LA_bits=None, LB_bits=None):
     return Y
 
 
+def _packed_dropped_lora(values, meta, scale, T_bits, W_bits, LA_bits, K):
+    return orc_packed_orig(values, meta, scale, None, W_bits, None, K)
+
+
+def _packed_lora_scaled_by_s(values, meta, scale, T_bits, W_bits, LA_bits, K):
+    # s applied after the LoRA term: s (X~ W^T + T LA^T)
+    Y = orc_packed_orig(values, meta, scale, T_bits, W_bits, LA_bits, K)
+    if T_bits is not None and LA_bits is not None:
+        Yr = orc.decode_bf16(T_bits) @ orc.decode_bf16(LA_bits).T
+        Y = Y + (np.asarray(scale, dtype=np.float64)[:, None] - 1.0) * Yr
+    return Y
+
+
+def _packed_lora_transposed_la(values, meta, scale, T_bits, W_bits, LA_bits, K):
+    Y = orc_packed_orig(values, meta, scale, None, W_bits, None, K)
+    if T_bits is not None and LA_bits is not None:
+        LA = orc.decode_bf16(LA_bits)
+        Y = Y + orc.decode_bf16(T_bits) @ np.flip(LA, axis=1).T
+    return Y
+
+
 orc_norm_scale_orig = orc.norm_scale
 orc_linear_orig = orc.linear_sparse_lora
+orc_packed_orig = orc.linear_from_packed
 
 MUTATIONS = {
     "ties_to_higher_index": ("select_top2_of_4", _ties_to_higher_index),
@@ -119,6 +142,9 @@ MUTATIONS = {
     "dropped_lora": ("linear_sparse_lora", _layer_dropped_lora),
     "negated_lora": ("linear_sparse_lora", _layer_negated_lora),
     "misoriented_lora_up": ("linear_sparse_lora", _layer_lora_la_lb_swapped_roles),
+    "packed_dropped_lora": ("linear_from_packed", _packed_dropped_lora),
+    "packed_lora_scaled_by_s": ("linear_from_packed", _packed_lora_scaled_by_s),
+    "packed_lora_rank_order_flipped": ("linear_from_packed", _packed_lora_transposed_la),
 }
 
 

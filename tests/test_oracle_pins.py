@@ -296,6 +296,40 @@ def test_packed_path_equals_layer():
     np.testing.assert_allclose(Y_packed, Y_ref, rtol=1e-13)
 
 
+def test_packed_path_with_lora_brute_force():
+    """linear_from_packed with its LoRA term: small-integer X and LB make
+    T = X LB^T exactly representable in bf16, so the packed path given the
+    packed operand, s and that T must reproduce the whole layer, which is
+    summed here by exact rational brute force from X.  The LoRA term is made
+    comparable to the sparse term and s > 1 on every row, so a dropped,
+    negated, s-scaled or mis-oriented T LA^T term fails."""
+    rng = np.random.default_rng(21)
+    M, K, N, R = 3, 16, 5, 4
+    x = rng.integers(-3, 4, size=(M, K)).astype(np.float32)
+    x[:, 0::4] = np.where(x[:, 0::4] == 0, 1.0, x[:, 0::4])   # >= 3 nonzeros in every group,
+    x[:, 1::4] = np.where(x[:, 1::4] == 0, -2.0, x[:, 1::4])  # so s > 1 on every row
+    x[:, 2::4] = np.where(x[:, 2::4] == 0, 3.0, x[:, 2::4])
+    Xb = bf16_bits_from_f32(x)
+    LB = bf16_bits_from_f32(rng.integers(-1, 2, size=(R, K)).astype(np.float32))
+    LA = bf16_bits_from_f32(rng.choice([-1.0, -0.5, 0.5, 1.0], size=(N, R)).astype(np.float32))
+    W = bf16_bits_from_f32((rng.standard_normal((N, K)) * 0.25).astype(np.float32))
+    res = orc.sparsify(Xb, LB)
+    assert np.all(res.scale > 1.0)
+    T_exact = [[sum(frac_of_bf16(Xb[m, k]) * frac_of_bf16(LB[r, k]) for k in range(K))
+                for r in range(R)] for m in range(M)]
+    assert all(t.denominator == 1 and abs(t) <= 256 for row in T_exact for t in row)
+    T_bits = bf16_bits_from_f32(np.array([[float(t) for t in row] for row in T_exact],
+                                         dtype=np.float32))
+    assert all(frac_of_bf16(T_bits[m, r]) == T_exact[m][r] for m in range(M) for r in range(R))
+    Y = orc.linear_from_packed(res.values, res.meta, res.scale, T_bits, W, LA, K)
+    Y_bf = brute_force_layer(Xb, W, LA, LB)
+    # the LoRA part is a sizeable share of every row
+    Yr = np.array([[float(sum(T_exact[m][r] * frac_of_bf16(LA[n, r]) for r in range(R)))
+                    for n in range(N)] for m in range(M)])
+    assert np.all(np.linalg.norm(Yr, axis=1) > 0.2 * np.linalg.norm(Y_bf, axis=1))
+    np.testing.assert_allclose(Y, Y_bf, rtol=1e-12, atol=1e-12)
+
+
 def test_meta_pack_unpack_round_trip():
     Xb = make_activation("heavy", 5, 128, seed=12)
     idx = orc.select_top2_of_4(Xb)
