@@ -19,7 +19,9 @@ LYNX_OK = 0
 STATUS_NAMES = {
     0: "LYNX_OK", 1: "LYNX_ERR_NULL", 2: "LYNX_ERR_SHAPE", 3: "LYNX_ERR_ALIGN",
     4: "LYNX_ERR_WORKSPACE", 5: "LYNX_ERR_DEVICE", 6: "LYNX_ERR_UNSUPPORTED_DEVICE",
+    7: "LYNX_ERR_SCRATCH",
 }
+SCRATCH_BYTES = 64 << 20  # LYNX_SCRATCH_BYTES
 
 LAYER_SPARSE_LORA, LAYER_DENSE = 0, 1
 
@@ -43,6 +45,7 @@ SIGNATURES = {
     "lynx_linear_sparse_lora": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "lynx_linear_sparse_lora_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                             _P]),
+    "lynx_linear_sparse_lora_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
     "lynx_linear_dense": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "lynx_sequence_workspace_bytes": (_SZ, [_LP, _I64]),
     "lynx_linear_sequence": (_I, [_LP, _I64, _P, _SZ, _P]),
@@ -174,6 +177,27 @@ def linear_sparse_lora(X, W, LA=None, LB=None, Y=None, workspace=None):
                                          R, _ptr(workspace), workspace.numel(),
                                          _stream(X.device)),
            "lynx_linear_sparse_lora")
+    return Y
+
+
+def linear_sparse_lora_noalloc(X, W, LA=None, LB=None, Y=None):
+    """Y = S(X) W^T + X (LA LB)^T with the library's static scratch array as
+    workspace (lynx_linear_sparse_lora_noalloc): the C call allocates nothing.
+    Pass Y to keep this wrapper from allocating it."""
+    M, K = X.shape
+    N = W.shape[0]
+    R = 0 if LA is None else LA.shape[1]
+    _need(X, torch.bfloat16, (M, K), "X")
+    _need(W, torch.bfloat16, (N, K), "W")
+    if R > 0:
+        _need(LA, torch.bfloat16, (N, R), "LA")
+        _need(LB, torch.bfloat16, (R, K), "LB")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _need(Y, torch.bfloat16, (M, N), "Y")
+    _check(lib().lynx_linear_sparse_lora_noalloc(_ptr(X), _ptr(W), _ptr(LA), _ptr(LB), _ptr(Y),
+                                                 M, N, K, R, _stream(X.device)),
+           "lynx_linear_sparse_lora_noalloc")
     return Y
 
 

@@ -145,6 +145,10 @@ const char* lynx_status_string(lynx_status s) {
         case LYNX_ERR_DEVICE: return "LYNX_ERR_DEVICE: a HIP call or kernel launch failed";
         case LYNX_ERR_UNSUPPORTED_DEVICE:
             return "LYNX_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950";
+        case LYNX_ERR_SCRATCH:
+            return "LYNX_ERR_SCRATCH: the problem needs more workspace than the library's "
+                   "static scratch array holds (64 MiB); call lynx_linear_sparse_lora with a "
+                   "workspace instead";
     }
     return "LYNX_ERR_UNKNOWN";
 }

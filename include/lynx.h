@@ -78,7 +78,9 @@ typedef enum lynx_status {
     LYNX_ERR_ALIGN = 3,              /* a pointer is not 16-byte aligned */
     LYNX_ERR_WORKSPACE = 4,          /* workspace is NULL or too small */
     LYNX_ERR_DEVICE = 5,             /* a HIP call or a kernel launch failed */
-    LYNX_ERR_UNSUPPORTED_DEVICE = 6  /* the current device is not gfx950 */
+    LYNX_ERR_UNSUPPORTED_DEVICE = 6, /* the current device is not gfx950 */
+    LYNX_ERR_SCRATCH = 7             /* the problem does not fit the static scratch array
+                                        of lynx_linear_sparse_lora_noalloc */
 } lynx_status;
 
 /* Human-readable name of a status; never NULL. */
@@ -124,6 +126,34 @@ lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W,
                                     int64_t M, int64_t N, int64_t K, int64_t R,
                                     void* workspace, size_t workspace_bytes,
                                     lynx_stream_t stream);
+
+/*
+ * lynx_linear_sparse_lora_noalloc - lynx_linear_sparse_lora without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same inputs, output, kernels and results as
+ * lynx_linear_sparse_lora; the packed operand, s and T go to a static device
+ * array of the library (64 MiB per device, LYNX_SCRATCH_BYTES), allocated
+ * when the library's code is loaded on a device and held until the process
+ * ends.  The call itself allocates nothing, on the device or the host.
+ *   - Problems whose lynx_workspace_bytes(M, K, R) exceeds LYNX_SCRATCH_BYTES
+ *     return LYNX_ERR_SCRATCH (e.g. M = 4096 fits up to K = 12288 with
+ *     R = 64; M = 9216 fits up to K = 6144).
+ *   - Every call on a device shares that device's array, which keeps the last
+ *     call's contents (each call writes every byte it reads before reading
+ *     it).  Calls that overlap on one device - on different streams, or from
+ *     different host threads without ordering - race on the array and give
+ *     undefined results; calls on one stream are ordered and safe.
+ *   - The first call on each device looks up the array's device address
+ *     (hipGetSymbolAddress) and keeps it; a failure there returns
+ *     LYNX_ERR_DEVICE.
+ */
+#define LYNX_SCRATCH_BYTES ((size_t)64 << 20)
+
+lynx_status lynx_linear_sparse_lora_noalloc(const uint16_t* X, const uint16_t* W,
+                                            const uint16_t* LA, const uint16_t* LB, uint16_t* Y,
+                                            int64_t M, int64_t N, int64_t K, int64_t R,
+                                            lynx_stream_t stream);
 
 /*
  * lynx_linear_sparse_lora_packed - the GEMM half of the layer on an already

@@ -14,7 +14,7 @@ import pytest
 from activation_sparse_gemm_amd import _abi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE, UNSUPPORTED = range(7)
+OK, NULL, SHAPE, ALIGN, WORKSPACE, DEVICE, UNSUPPORTED, SCRATCH = range(8)
 
 A = 0x10000  # a fake, 16-byte-aligned address: validation fails before any use
 B = 0x20000
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert _abi.status_string(s).startswith(_abi.STATUS_NAMES[s])
     assert "UNKNOWN" in _abi.status_string(99)
 
@@ -94,6 +94,37 @@ def test_linear_validation(kw, status):
 def test_linear_workspace_exact_boundary():
     need = _abi.workspace_bytes(16, 128, 16)
     assert call_linear(wsb=need - 1) == WORKSPACE
+
+
+def call_noalloc(X=A, W=A, LA=A, LB=A, Y=A, M=16, N=16, K=128, R=16):
+    return _abi.lib().lynx_linear_sparse_lora_noalloc(X, W, LA, LB, Y, M, N, K, R, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=192), SHAPE), (dict(R=17), SHAPE), (dict(M=1 << 25), SHAPE),
+    (dict(W=None), NULL), (dict(LB=None), NULL), (dict(Y=A + 2), ALIGN),
+    (dict(M=0), OK), (dict(N=0), OK),
+    # the static scratch array holds LYNX_SCRATCH_BYTES = 64 MiB
+    (dict(M=9216, K=12288, R=64), SCRATCH), (dict(M=8192, K=8192, R=0), SCRATCH),
+])
+def test_noalloc_validation(kw, status):
+    assert call_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_is_the_workspace_size():
+    """A problem is accepted exactly when its workspace fits the array."""
+    import torch
+    fits = [(4096, 12288, 64), (4096, 3072, 64), (7248, 8192, 16), (9520, 6144, 64)]
+    too_big = [(9216, 12288, 64), (7249, 8192, 16), (9521, 6144, 64)]
+    for M, K, R in fits:
+        assert 0 < _abi.workspace_bytes(M, K, R) <= _abi.SCRATCH_BYTES
+    for M, K, R in too_big:
+        assert _abi.workspace_bytes(M, K, R) > _abi.SCRATCH_BYTES
+        assert call_noalloc(M=M, K=K, R=R) == SCRATCH
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
+    for M, K, R in fits:
+        assert call_noalloc(M=M, K=K, R=R) == UNSUPPORTED
 
 
 def call_packed(v=A, m=A, s=A, T=A, W=A, LA=A, Y=A, M=16, N=16, K=128, R=16):
