@@ -50,6 +50,7 @@ SIGNATURES = {
     "lynx_sequence_workspace_bytes": (_SZ, [_LP, _I64]),
     "lynx_linear_sequence": (_I, [_LP, _I64, _P, _SZ, _P]),
     "lynx_probe_mfma": (_I, [_I, _I, _P, _P, _P, _P, _P]),
+    "lynx_probe_mfma_rate": (_I, [_I, _I, _I, _P, _P, _P]),
 }
 
 
@@ -276,6 +277,29 @@ def linear_sequence(layers: list, workspace=None):
                                       0 if workspace is None else workspace.numel(),
                                       _stream(dev)),
            "lynx_linear_sequence")
+
+
+# dense-equivalent flops of one instruction of each probe kind: smfmac
+# 16x16x64, smfmac 32x32x32, mfma 16x16x32, mfma 32x32x16 (bf16)
+PROBE_NAMES = ("v_smfmac_f32_16x16x64_bf16", "v_smfmac_f32_32x32x32_bf16",
+               "v_mfma_f32_16x16x32_bf16", "v_mfma_f32_32x32x16_bf16")
+PROBE_FLOPS = (2 * 16 * 16 * 64, 2 * 32 * 32 * 32, 2 * 16 * 16 * 32, 2 * 32 * 32 * 16)
+
+
+def probe_mfma_rate(which: int, iters: int, grid: int, device=None) -> dict:
+    """Runs lynx_probe_mfma_rate once on torch's current stream and returns the
+    event-timed duration with the per-wave stamps (no arithmetic of the layer)."""
+    dev = torch.device("cuda") if device is None else device
+    sink = torch.empty((grid * 256,), dtype=torch.float32, device=dev)
+    stamps = torch.zeros((grid * 4, 2), dtype=torch.int64, device=dev)
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    _check(lib().lynx_probe_mfma_rate(which, iters, grid, _ptr(sink), _ptr(stamps), _stream(dev)),
+           "lynx_probe_mfma_rate")
+    end.record()
+    torch.cuda.synchronize()
+    return {"ms": start.elapsed_time(end), "stamps": stamps.cpu().numpy()}
 
 
 def probe_mfma(which: int, abid: int, a: torch.Tensor, b: torch.Tensor,

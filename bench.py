@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--summarize-mfma", metavar="SQ_DIR",
                    help="write profiles/mfma_busy_<workload>.json from a rocprofv3 --pmc run of "
                         "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE and exit")
+    p.add_argument("--mfma-peak", action="store_true",
+                   help="measure the bf16 matrix-instruction issue rates and the clock under "
+                        "that load (lynx_probe_mfma_rate, one wave per SIMD on every compute unit) "
+                        "and exit")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into profiles/traffic_<workload>.json")
@@ -289,8 +293,40 @@ def traffic_for(kernel_src: str, workload: str):
     return rec.get("bytes_per_launch") if rec.get("kernel_sha") == source_sha(kernel_src) else None
 
 
+def mfma_peak() -> dict:
+    """Measured peak of each bf16 matrix instruction the kernels use: every
+    compute unit runs 4 waves (one per SIMD) of back-to-back instructions.
+    Reports cycles per instruction and the shader clock from the waves' own
+    counters, and the chip-wide dense-equivalent TFLOP/s from HIP events."""
+    import numpy as np
+    import torch
+
+    from activation_sparse_gemm_amd import _abi
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {"cus": cus, "simds": 4 * cus, "instructions": {}}
+    for which, name in enumerate(_abi.PROBE_NAMES):
+        iters = 4096 if which in (0, 2) else 2048
+        _abi.probe_mfma_rate(which, 64, cus)          # warm-up
+        runs = [_abi.probe_mfma_rate(which, iters, cus) for _ in range(5)]
+        ms = float(np.median([r["ms"] for r in runs]))
+        st = np.concatenate([r["stamps"] for r in runs]).astype(np.float64)
+        cpi = float(np.median(st[:, 0])) / (16 * iters)
+        mhz = float(np.median(100.0 * st[:, 0] / np.maximum(st[:, 1], 1)))
+        n_instr = 4 * cus * 16 * iters
+        tf = n_instr * _abi.PROBE_FLOPS[which] / (ms * 1e-3) / 1e12
+        out["instructions"][name] = {
+            "cycles_per_instruction": round(cpi, 2), "clock_mhz": round(mhz, 1),
+            "tflops_dense_equiv": round(tf, 1),
+            "tflops_at_2400mhz": round(4 * cus * _abi.PROBE_FLOPS[which] / cpi * 2.4e9 / 1e12, 1),
+            "ms": round(ms, 4), "iters": iters}
+    return out
+
+
 def main():
     args = parse()
+    if args.mfma_peak:
+        print(json.dumps(mfma_peak()))
+        return
     if args.summarize_mfma:
         print(json.dumps(summarize_mfma(args.summarize_mfma, args.workload)))
         return

@@ -33,6 +33,22 @@ extern "C" {
 lynx_status lynx_probe_mfma(int which, int abid, const uint16_t* a, const uint16_t* b,
                             const uint32_t* idx, float* d, lynx_stream_t stream);
 
+/*
+ * Matrix-instruction issue rate and clock: `grid` workgroups of 4 waves (one
+ * wave per SIMD when grid = the compute-unit count); every wave issues
+ * iters * 16 instructions `which` (numbered as above) over 4 independent
+ * accumulators, stamping the shader-clock counter (s_memtime) and the 100 MHz
+ * real-time counter (s_memrealtime) before and after.
+ *   sink   [grid * 256] fp32 (written, keeps the work alive);
+ *   stamps [grid * 4][2] uint64: per wave, shader cycles and real-time ticks
+ *          spent in the loop.
+ * Cycles per instruction = stamps[.][0] / (16 iters); the clock in MHz =
+ * 100 * stamps[.][0] / stamps[.][1].  This measures the peak that the page's
+ * sparse-unit speedups (주요 결과) rest on, on this device.
+ */
+lynx_status lynx_probe_mfma_rate(int which, int iters, int grid, float* sink, uint64_t* stamps,
+                                 lynx_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

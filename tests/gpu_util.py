@@ -77,3 +77,65 @@ def dump_dir():
     if d:
         os.makedirs(d, exist_ok=True)
     return d
+
+
+# ---- calls with poisoned outputs -------------------------------------------
+# Every output buffer (and the layer's workspace) is filled with a value no
+# kernel writes from finite inputs before each call: a bf16 NaN, a fp32 NaN,
+# meta bytes 0xFF (code 3|3<<2, which the format never uses).  An element the
+# kernels fail to write then fails the parity checks instead of passing on
+# whatever an earlier call left in a recycled buffer.
+NAN_BF16_BITS = 0x7FC0
+
+
+def nan_bf16(shape) -> torch.Tensor:
+    return torch.full(shape, NAN_BF16_BITS, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+
+
+def poisoned_bytes(n: int) -> torch.Tensor:
+    return torch.full((max(n, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+def sparse_lora(X, W, LA=None, LB=None):
+    import activation_sparse_gemm_amd as lynx
+    (M, K), N = X.shape, W.shape[0]
+    R = 0 if LA is None else LA.shape[1]
+    return lynx.linear_sparse_lora(X, W, LA, LB, Y=nan_bf16((M, N)),
+                                   workspace=poisoned_bytes(lynx.workspace_bytes(M, K, R)))
+
+
+def sparse_lora_noalloc(X, W, LA=None, LB=None):
+    import activation_sparse_gemm_amd as lynx
+    return lynx.linear_sparse_lora_noalloc(X, W, LA, LB, Y=nan_bf16((X.shape[0], W.shape[0])))
+
+
+def dense(X, W):
+    import activation_sparse_gemm_amd as lynx
+    return lynx.linear_dense(X, W, Y=nan_bf16((X.shape[0], W.shape[0])))
+
+
+def packed(values, meta, scale, T, W, LA=None):
+    import activation_sparse_gemm_amd as lynx
+    return lynx.linear_sparse_lora_packed(values, meta, scale, T, W, LA,
+                                          Y=nan_bf16((scale.shape[0], W.shape[0])))
+
+
+def sparsify(X, LB=None):
+    import activation_sparse_gemm_amd as lynx
+    M, K = X.shape
+    Mp = lynx.padded_rows(M) if hasattr(lynx, "padded_rows") else (M + 15) // 16 * 16
+    out = dict(values=nan_bf16((Mp * K // 2,)),
+               meta=torch.full((Mp * K // 8,), 0xFF, dtype=torch.uint8, device="cuda"),
+               scale=torch.full((M,), float("nan"), dtype=torch.float32, device="cuda"))
+    if LB is not None:
+        out["T"] = nan_bf16((M, LB.shape[0]))
+    return lynx.sparsify(X, LB, out=out)
+
+
+def sequence(layers):
+    """lynx_linear_sequence with every layer's Y and the workspace poisoned."""
+    import activation_sparse_gemm_amd as lynx
+    for d in layers:
+        d["Y"].view(torch.int16).fill_(NAN_BF16_BITS)
+    ws = poisoned_bytes(lynx.sequence_workspace_bytes(layers))
+    lynx.linear_sequence(layers, workspace=ws)

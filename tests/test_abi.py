@@ -192,6 +192,11 @@ def test_probe_validation():
     assert L.lynx_probe_mfma(0, 2, A, A, A, A, None) == SHAPE
     assert L.lynx_probe_mfma(0, 0, A, A, None, A, None) == NULL
     assert L.lynx_probe_mfma(1, 0, A + 1, A, A, A, None) == ALIGN
+    assert L.lynx_probe_mfma_rate(4, 16, 256, A, B, None) == SHAPE
+    assert L.lynx_probe_mfma_rate(0, 0, 256, A, B, None) == SHAPE
+    assert L.lynx_probe_mfma_rate(0, 16, 0, A, B, None) == SHAPE
+    assert L.lynx_probe_mfma_rate(1, 16, 256, None, B, None) == NULL
+    assert L.lynx_probe_mfma_rate(1, 16, 256, A, B + 8, None) == ALIGN
 
 
 def test_valid_arguments_without_gpu_report_unsupported_device():

@@ -45,14 +45,15 @@ def test_fidelity_claims_on_synthetic_layers(kind):
 def test_gpu_path_reproduces_the_fitted_method():
     import torch
 
-    import activation_sparse_gemm_amd as lynx
+    import activation_sparse_gemm_amd as lynx  # noqa: F401
+    import tests.gpu_util as gu
     from tests.gpu_util import ROW_REL_TOL, dev, host_f64, say
 
     r = fs.study("heavy", K=1024, N=512, M_cal=8192, M_eval=2048, R=64)
     LA_bits, LB_bits = fs.lora_bits(*r["_lora"])
     Xe, W = r["_eval"]
     say("fidelity: fitted LoRA through the GPU path")
-    Y = host_f64(lynx.linear_sparse_lora(dev(Xe), dev(W), dev(LA_bits), dev(LB_bits)))
+    Y = host_f64(gu.sparse_lora(dev(Xe), dev(W), dev(LA_bits), dev(LB_bits)))
     torch.cuda.synchronize()
     Yref = orc.linear_sparse_lora(Xe, W, LA_bits, LB_bits)
     rows = np.linalg.norm(Y - Yref, axis=1) / np.linalg.norm(Yref, axis=1)

@@ -23,6 +23,7 @@ import pytest
 import torch
 
 import activation_sparse_gemm_amd as lynx
+import tests.gpu_util as gu
 from oracle import lynx_oracle as orc
 from tests.gpu_util import ROW_REL_TOL, dev, host_f64, report, row_rel_err, sample_rows, say
 from workloads import bf16_bits_from_f32, make_activation, make_layer, make_weights
@@ -87,7 +88,7 @@ def test_scale_spanning_one_to_sqrt2_with_lora(M, K, N):
     LA, LB = lora_weights(N, K, 64, 0.05, seed=13)
     rows = checked_rows(M)
     say(f"edges: s in [1, sqrt2] with LoRA M={M} K={K} N={N}")
-    Y = lynx.linear_sparse_lora(dev(Xb), dev(W), dev(LA), dev(LB))
+    Y = gu.sparse_lora(dev(Xb), dev(W), dev(LA), dev(LB))
     torch.cuda.synchronize()
     Yg = host_f64(Y)[rows]
     del Y
@@ -113,7 +114,7 @@ def test_zero_weight_leaves_lora(M, K, N):
     W0 = np.zeros((N, K), dtype=np.uint16)
     rows = checked_rows(M)
     say(f"edges: W = 0 M={M} K={K} N={N}")
-    Y = lynx.linear_sparse_lora(dev(Xb), dev(W0), dev(LA), dev(LB))
+    Y = gu.sparse_lora(dev(Xb), dev(W0), dev(LA), dev(LB))
     torch.cuda.synchronize()
     Yg = host_f64(Y)[rows]
     del Y
@@ -132,8 +133,8 @@ def test_two_sparse_input_without_lora_is_dense(M, K, N):
     rows = checked_rows(M)
     say(f"edges: 2-sparse input, LA = 0 M={M} K={K} N={N}")
     Xd, Wd = dev(Xb), dev(W)
-    Y = lynx.linear_sparse_lora(Xd, Wd, dev(LA0), dev(LB))
-    Yd = lynx.linear_dense(Xd, Wd)
+    Y = gu.sparse_lora(Xd, Wd, dev(LA0), dev(LB))
+    Yd = gu.dense(Xd, Wd)
     torch.cuda.synchronize()
     Yg, Ydg = host_f64(Y), host_f64(Yd)
     del Xd, Wd, Y, Yd

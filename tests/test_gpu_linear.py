@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import activation_sparse_gemm_amd as lynx
+import tests.gpu_util as gu
 from oracle import lynx_oracle as orc
 from tests.gpu_util import ROW_REL_TOL, dev, host_f64, report, sample_rows, say
 from workloads import CONFIGS, bf16_bits_from_f32, make_activation, make_layer, make_weights
@@ -44,7 +45,7 @@ def test_linear_sparse_lora_shapes(M, K, N, R):
     L = make_layer(M, K, N, "heavy", seed=M + N, R=max(R, 16))
     LA, LB = (None, None) if R == 0 else (L.LA, L.LB)
     say(f"linear_sparse_lora M={M} K={K} N={N} R={R}")
-    Y = lynx.linear_sparse_lora(dev(L.X), dev(L.W), None if R == 0 else dev(LA),
+    Y = gu.sparse_lora(dev(L.X), dev(L.W), None if R == 0 else dev(LA),
                                 None if R == 0 else dev(LB))
     torch.cuda.synchronize()
     check(Y, orc.linear_sparse_lora(L.X, L.W, LA, LB), f"sparse_lora {M}x{K}->{N} R{R}")
@@ -58,8 +59,8 @@ def test_ragged_wide_tiles_sampled_rows():
     L = make_layer(M, K, N, "heavy", seed=5, R=R)
     rows = np.unique(np.concatenate([sample_rows(M, n=24, seed=5), np.arange(M - 40, M)]))
     say(f"ragged wide tiles M={M} K={K} N={N} R={R}")
-    Y = lynx.linear_sparse_lora(dev(L.X), dev(L.W), dev(L.LA), dev(L.LB))
-    Yd = lynx.linear_dense(dev(L.X), dev(L.W))
+    Y = gu.sparse_lora(dev(L.X), dev(L.W), dev(L.LA), dev(L.LB))
+    Yd = gu.dense(dev(L.X), dev(L.W))
     torch.cuda.synchronize()
     check(torch.from_numpy(host_f64(Y)[rows]), orc.linear_sparse_lora(L.X[rows], L.W, L.LA, L.LB),
           "ragged wide sparse_lora")
@@ -75,7 +76,7 @@ def test_linear_packed_entry(M, K, N, R):
     scale = torch.from_numpy(ref.scale.astype(np.float32)).cuda()
     meta = torch.from_numpy(ref.meta_stored()).cuda()
     say(f"packed M={M} K={K} N={N} R={R}")
-    Y = lynx.linear_sparse_lora_packed(dev(ref.values_stored()), meta, scale, dev(T_bits),
+    Y = gu.packed(dev(ref.values_stored()), meta, scale, dev(T_bits),
                                        dev(L.W), dev(L.LA))
     torch.cuda.synchronize()
     Yref = orc.linear_from_packed(ref.values, ref.meta, ref.scale.astype(np.float32), T_bits,
@@ -89,7 +90,7 @@ def test_linear_packed_entry(M, K, N, R):
 def test_linear_dense_shapes(M, K, N):
     L = make_layer(M, K, N, "heavy", seed=M + K + N, R=16)
     say(f"dense M={M} K={K} N={N}")
-    Y = lynx.linear_dense(dev(L.X), dev(L.W))
+    Y = gu.dense(dev(L.X), dev(L.W))
     torch.cuda.synchronize()
     check(Y, orc.linear_dense(L.X, L.W), f"dense {M}x{K}->{N}")
 
@@ -105,8 +106,8 @@ def test_identity_two_sparse_input_without_lora_is_dense():
     Xb = bf16_bits_from_f32(x)
     W, LA, LB = make_weights(N, K, 64, seed=4)
     say("identity: 2-sparse input, LA = 0")
-    Y = lynx.linear_sparse_lora(dev(Xb), dev(W), dev(np.zeros_like(LA)), dev(LB))
-    Yd = lynx.linear_dense(dev(Xb), dev(W))
+    Y = gu.sparse_lora(dev(Xb), dev(W), dev(np.zeros_like(LA)), dev(LB))
+    Yd = gu.dense(dev(Xb), dev(W))
     torch.cuda.synchronize()
     check(Y, orc.linear_dense(Xb, W), "identity vs oracle dense")
     assert torch.equal(Y.view(torch.int16), Yd.view(torch.int16)) or \
@@ -116,7 +117,7 @@ def test_identity_two_sparse_input_without_lora_is_dense():
 def test_identity_zero_weight_leaves_lora():
     L = make_layer(130, 512, 96, "heavy", seed=5)
     say("identity: W = 0")
-    Y = lynx.linear_sparse_lora(dev(L.X), dev(np.zeros_like(L.W)), dev(L.LA), dev(L.LB))
+    Y = gu.sparse_lora(dev(L.X), dev(np.zeros_like(L.W)), dev(L.LA), dev(L.LB))
     torch.cuda.synchronize()
     Yref = (orc.decode_bf16(L.X) @ orc.decode_bf16(L.LB).T) @ orc.decode_bf16(L.LA).T
     check(Y, Yref, "W = 0")
@@ -128,7 +129,7 @@ def test_plus_minus_one_input_scale_sqrt2():
     Xb = np.where(rng.random((M, K)) < 0.5, 0x3F80, 0xBF80).astype(np.uint16)
     W, LA, LB = make_weights(N, K, 64, seed=6)
     say("+-1 input")
-    Y = lynx.linear_sparse_lora(dev(Xb), dev(W), dev(LA), dev(LB))
+    Y = gu.sparse_lora(dev(Xb), dev(W), dev(LA), dev(LB))
     torch.cuda.synchronize()
     check(Y, orc.linear_sparse_lora(Xb, W, LA, LB), "+-1 input")
 
@@ -150,8 +151,8 @@ def test_full_size_layers(cfg, layer):
     rows = sample_rows(M, n=24, seed=layer)
     X, W, LA, LB = dev(L.X), dev(L.W), dev(L.LA), dev(L.LB)
     say(f"full {cfg}[{layer}] M={M} K={K} N={N}")
-    Y = lynx.linear_sparse_lora(X, W, LA, LB)
-    Yd = lynx.linear_dense(X, W)
+    Y = gu.sparse_lora(X, W, LA, LB)
+    Yd = gu.dense(X, W)
     torch.cuda.synchronize()
     Yh = host_f64(Y)
     Ydh = host_f64(Yd)[rows]

@@ -143,3 +143,26 @@ def test_mfma_32x32x16_layout():
         A[l % 32, 8 * (l // 32): 8 * (l // 32) + 8] = a[l]
         B[8 * (l // 32): 8 * (l // 32) + 8, l % 32] = b[l]
     np.testing.assert_array_equal(d, acc_32(A @ B))
+
+
+def test_matrix_instruction_issue_rates():
+    """The peaks the roofline uses: the 32x32 bf16 forms issue once per 32
+    cycles per SIMD, the 2:4 one doing twice the dense one's work, and the
+    16x16x64 2:4 form about once per 16; the shader clock under that load
+    lies within the chip's range."""
+    import numpy as np
+
+    from activation_sparse_gemm_amd import _abi
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    expect = {0: (15.5, 18.5), 1: (31.5, 33.5), 3: (31.5, 33.5)}
+    for which, (lo, hi) in expect.items():
+        say(f"issue rate of {_abi.PROBE_NAMES[which]}")
+        r = _abi.probe_mfma_rate(which, 1024, cus)
+        st = r["stamps"].astype(np.float64)
+        assert np.all(st[:, 0] > 0) and np.all(st[:, 1] > 0)
+        cpi = float(np.median(st[:, 0])) / (16 * 1024)
+        mhz = float(np.median(100.0 * st[:, 0] / st[:, 1]))
+        say(f"  {cpi:.2f} cycles per instruction at {mhz:.0f} MHz")
+        assert lo <= cpi <= hi, cpi
+        assert 800.0 <= mhz <= 2500.0, mhz
+    assert _abi.PROBE_FLOPS[1] == 2 * _abi.PROBE_FLOPS[3]

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import activation_sparse_gemm_amd as lynx
+import tests.gpu_util as gu
 from oracle import lynx_oracle as orc
 from tests.gpu_util import ROW_REL_TOL, dev, host_f64, report, sample_rows, say
 from workloads import BLOCK_LAYER_NAMES, make_config, make_layer
@@ -38,7 +39,7 @@ def test_mixed_small_sequence():
     Ls = [make_layer(M, K, N, "heavy", seed=11 + i) for i, (M, K, N, _) in enumerate(specs)]
     layers = [as_device(L, sk) for L, (_, _, _, sk) in zip(Ls, specs)]
     say("sequence of 6 layers, two skipped")
-    lynx.linear_sequence(layers)
+    gu.sequence(layers)
     torch.cuda.synchronize()
     refs = orc.linear_sequence([(L.X, L.W, L.LA, L.LB, sk) for L, (_, _, _, sk) in zip(Ls, specs)])
     for i, (d, ref) in enumerate(zip(layers, refs)):
@@ -49,9 +50,9 @@ def test_mixed_small_sequence():
         if not d["Y"].numel():
             continue
         if d["dense"]:
-            Y1 = lynx.linear_dense(d["X"], d["W"])
+            Y1 = gu.dense(d["X"], d["W"])
         else:
-            Y1 = lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"])
+            Y1 = gu.sparse_lora(d["X"], d["W"], d["LA"], d["LB"])
         torch.cuda.synchronize()
         assert torch.equal(Y1.view(torch.int16), d["Y"].view(torch.int16))
 
@@ -62,7 +63,7 @@ def test_block_sequence_sampled_rows(skip):
     flags = [name in skip for name in BLOCK_LAYER_NAMES]
     layers = [as_device(L, sk) for L, sk in zip(Ls, flags)]
     say(f"block sequence, skipped: {skip or 'none'}")
-    lynx.linear_sequence(layers)
+    gu.sequence(layers)
     torch.cuda.synchronize()
     for i, (L, d, sk) in enumerate(zip(Ls, layers, flags)):
         rows = sample_rows(L.M, n=16, seed=i)

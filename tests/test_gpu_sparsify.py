@@ -10,6 +10,7 @@ import pytest
 import torch
 
 import activation_sparse_gemm_amd as lynx
+import tests.gpu_util as gu
 from oracle import lynx_oracle as orc
 from tests.gpu_util import (ROW_REL_TOL, SCALE_REL_TOL, dev, host_bits, host_f64, report,
                             row_rel_err, say)
@@ -22,7 +23,7 @@ def check_sparsify(Xb, LBb, label):
     """Stored packed operand (incl. padding rows) bit-exact, scale, T."""
     M, K = Xb.shape
     say(f"sparsify {label} M={M} K={K} R={0 if LBb is None else LBb.shape[0]}")
-    values, meta, scale, T = lynx.sparsify(dev(Xb), None if LBb is None else dev(LBb))
+    values, meta, scale, T = gu.sparsify(dev(Xb), None if LBb is None else dev(LBb))
     torch.cuda.synchronize()
     ref = orc.sparsify(Xb, LBb)
     np.testing.assert_array_equal(meta.cpu().numpy(), ref.meta_stored(), err_msg=f"{label}: meta")
@@ -109,8 +110,8 @@ def test_sparsify_is_deterministic():
     Xb = make_activation("heavy", 300, 3072, seed=7)
     LB = make_weights(8, 3072, 64, seed=7)[2]
     X, L = dev(Xb), dev(LB)
-    a = [t.clone() for t in lynx.sparsify(X, L)]
-    b = lynx.sparsify(X, L)
+    a = [t.clone() for t in gu.sparsify(X, L)]
+    b = gu.sparsify(X, L)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,
@@ -124,7 +125,7 @@ def test_sparsify_full_size(M, K, kind):
     Xb = make_activation(kind, M, K, seed=0)
     LB = make_weights(8, K, 64, seed=0)[2]
     say(f"sparsify full {M}x{K} {kind}")
-    values, meta, scale, T = lynx.sparsify(dev(Xb), dev(LB))
+    values, meta, scale, T = gu.sparsify(dev(Xb), dev(LB))
     torch.cuda.synchronize()
     idx = orc.select_top2_of_4(Xb)
     np.testing.assert_array_equal(meta.cpu().numpy(),
@@ -183,7 +184,7 @@ def test_sparsify_extreme_rows_across_row_tiles(M):
                 special[m] = k
     rows = np.array(sorted(special))
     say(f"sparsify extreme rows M={M} K={K} R={R}: {len(rows)} special rows")
-    values, meta, scale, T = lynx.sparsify(dev(Xb), dev(LB))
+    values, meta, scale, T = gu.sparsify(dev(Xb), dev(LB))
     torch.cuda.synchronize()
     ref = orc.sparsify(Xb, LB)
     np.testing.assert_array_equal(meta.cpu().numpy(), ref.meta_stored(), err_msg="meta")
@@ -208,8 +209,8 @@ def test_sparsify_is_deterministic_three_row_tiles():
     LB = make_weights(8, 3072, 64, seed=9)[2]
     X, L = dev(Xb), dev(LB)
     say("sparsify determinism M=9000 K=3072 R=64 (3 row tiles per workgroup)")
-    a = [t.clone() for t in lynx.sparsify(X, L)]
-    b = lynx.sparsify(X, L)
+    a = [t.clone() for t in gu.sparsify(X, L)]
+    b = gu.sparsify(X, L)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.uint8) if x.dtype != torch.uint8 else x,

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import activation_sparse_gemm_amd as lynx
+import tests.gpu_util as gu
 from oracle import lynx_oracle as orc
 from tests.gpu_util import ROW_REL_TOL, dev, host_f64, report, sample_rows, say
 from workloads import make_layer
@@ -24,10 +25,10 @@ def check_against_workspace_entry(M, K, N, R, seed):
     X, W = dev(L.X), dev(L.W)
     LA, LB = (None, None) if R == 0 else (dev(L.LA), dev(L.LB))
     say(f"noalloc M={M} K={K} N={N} R={R}")
-    Yn = lynx.linear_sparse_lora_noalloc(X, W, LA, LB)
+    Yn = gu.sparse_lora_noalloc(X, W, LA, LB)
     torch.cuda.synchronize()
     say(f"workspace entry M={M} K={K} N={N} R={R}")
-    Yw = lynx.linear_sparse_lora(X, W, LA, LB)
+    Yw = gu.sparse_lora(X, W, LA, LB)
     torch.cuda.synchronize()
     assert torch.equal(Yn.view(torch.int16), Yw.view(torch.int16)), "Y differs from the workspace entry"
     rows = sample_rows(M, n=24, seed=seed)
