@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -62,6 +63,13 @@ def parse():
                    help="measure the bf16 matrix-instruction issue rates and the clock under "
                         "that load (lynx_probe_mfma_rate, one wave per SIMD on every compute unit) "
                         "and exit")
+    p.add_argument("--cpu-table", action="store_true",
+                   help="CPU baseline per workload: the oracle on bounded row samples of every "
+                        "workload, BLAS at one thread and at all cores, median of 3; print one "
+                        "JSON line and exit (no GPU)")
+    p.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                   help="no GPU: write profiles/trace_<workload>.md from a rocprofv3 --kernel-trace "
+                        "run of this benchmark and exit")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into profiles/traffic_<workload>.json")
@@ -171,13 +179,80 @@ def cpu_baseline(L, min_s=10.0, max_rows_growth=8.0, one_thread_s=6.0):
     return rec
 
 
-K2_SRC = os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc", "k_gemm.hip")
+def cpu_table(target_s=0.5, repeats=3) -> dict:
+    """The oracle (as it stands) on every workload, once with BLAS limited to
+    one thread and once with all cores.  A call costs a fixed part (decoding
+    the layer's W, LA, LB) plus a part linear in the rows of X (the layer is
+    row-independent), so each layer is timed on r and 2 r rows (median of
+    `repeats` calls each, r sized so the row part of a call is about
+    target_s) and the whole layer's time is fixed + M x per-row."""
+    import statistics
+
+    import threadpoolctl
+
+    from oracle import lynx_oracle as orc
+    from workloads import CONFIGS, make_config
+    info = threadpoolctl.threadpool_info()
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '')}".strip()
+                             for i in info if i.get("user_api") == "blas"})) or "unknown"
+    all_threads = max((i.get("num_threads", 1) for i in info), default=os.cpu_count())
+    out = {"cpu_model": cpu_model(), "os_cpu_count": os.cpu_count(), "blas": blas,
+           "threads_all": all_threads, "repeats": repeats, "workloads": {}}
+
+    def call(L, rows):
+        t0 = time.perf_counter()
+        orc.linear_sparse_lora(L.X[:rows], L.W, L.LA, L.LB)
+        return time.perf_counter() - t0
+
+    for name in CONFIGS:
+        layers = make_config(name)
+        flops = sum(L.dense_equiv_flops for L in layers)
+        rec = {"layers": [f"{L.M}x{L.K}->{L.N}" for L in layers],
+               "dense_equiv_gflop": round(flops / 1e9, 2)}
+        for label, limit in (("one_thread", 1), ("all_cores", all_threads)):
+            with threadpoolctl.threadpool_limits(limit):
+                total_s, sample = 0.0, []
+                for L in layers:
+                    r0 = min(64, max(1, L.M // 2))
+                    t1, t2 = call(L, r0), call(L, 2 * r0)
+                    per_row = max((t2 - t1) / r0, 1e-9)
+                    r = int(min(L.M // 2, max(r0, target_s / per_row)))
+                    a = statistics.median(call(L, r) for _ in range(repeats))
+                    b = statistics.median(call(L, 2 * r) for _ in range(repeats))
+                    per_row = max((b - a) / r, 0.0)
+                    fixed = max(a - r * per_row, 0.0)
+                    total_s += fixed + L.M * per_row
+                    sample.append(f"{r} and {2 * r} of {L.M} rows")
+            rec[label] = {"seconds_whole_workload": round(total_s, 3),
+                          "tflops": round(flops / total_s / 1e12, 5), "threads": limit,
+                          "sample": "; ".join(sample)}
+            print(f"cpu table: {name} {label}: {total_s:.2f} s", file=sys.stderr, flush=True)
+        out["workloads"][name] = rec
+    return out
+
+
+CSRC = os.path.join(ROOT, "activation_sparse_gemm_amd", "csrc")
+# the source files each profiled kernel is built from (its .hip and the
+# internal headers it includes): a counter record is used only while their
+# hash matches the one it was taken on
+KERNEL_SOURCES = {
+    "gemm_sparse32": ("k_gemm.hip", "lynx_tile.h", "lynx_dma.h", "lynx_internal.h"),
+    "gemm_dense32": ("k_gemm_dense.hip", "lynx_tile.h", "lynx_dma.h", "lynx_internal.h"),
+    "sparsify_kernel": ("k_sparsify.hip", "lynx_internal.h"),
+}
 COPY_MIB = 256
 
 
-def source_sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(kernel: str) -> str:
+    """Hash of the sources `kernel` is built from (None for a library kernel)."""
+    files = KERNEL_SOURCES.get(kernel)
+    if files is None:
+        return None
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def per_dispatch_kib(run_dir: str, counter: str) -> dict:
@@ -215,14 +290,27 @@ def summarize_traffic(fetch_dir: str, write_dir: str, workload: str) -> dict:
             raise SystemExit(f"expected one kernel matching {key!r}, found {hits}")
         return d[hits[0]]
 
+    def mean_over(d, key):
+        # mean per dispatch over every instantiation matching key (each layer
+        # of a workload is launched once per step)
+        hits = [k for k in d if key in k]
+        if not hits:
+            raise SystemExit(f"no kernel matching {key!r}")
+        return sum(d[k] for k in hits) / len(hits)
+
+    from workloads import CONFIGS
+    per_step = len(CONFIGS[workload]) if workload in CONFIGS else 1
     known_kib = COPY_MIB * 1024.0
     f_factor = known_kib / pick(fetch, "neg")
     w_factor = known_kib / pick(write, "neg")
-    f_bytes = pick(fetch, "gemm_sparse32") * 1024.0 * f_factor
-    w_bytes = pick(write, "gemm_sparse32") * 1024.0 * w_factor
-    rec = {"workload": workload, "kernel": "gemm_sparse32", "kernel_sha": source_sha(K2_SRC),
-           "fetch_bytes_per_launch": round(f_bytes), "write_bytes_per_launch": round(w_bytes),
-           "bytes_per_launch": round(f_bytes + w_bytes),
+    f_bytes = mean_over(fetch, "gemm_sparse32") * 1024.0 * f_factor * per_step
+    w_bytes = mean_over(write, "gemm_sparse32") * 1024.0 * w_factor * per_step
+    rec = {"workload": workload, "kernel": "gemm_sparse32", "kernel_sha": source_sha("gemm_sparse32"),
+           "launches_per_step": per_step,
+           "fetch_bytes_per_launch": round(f_bytes / per_step),
+           "write_bytes_per_launch": round(w_bytes / per_step),
+           "bytes_per_launch": round((f_bytes + w_bytes) / per_step),
+           "bytes_per_step": round(f_bytes + w_bytes),
            "copy_factor_fetch": round(f_factor, 4), "copy_factor_write": round(w_factor, 4),
            "commands": [f"rocprofv3 --pmc {c} -d <dir> -o run -- python3 bench.py --steps 3 "
                         f"--warmup 1 --no-cpu --sets 1 --copy-calibration --workload {workload}"
@@ -253,15 +341,16 @@ def summarize_mfma(sq_dir: str, workload: str) -> dict:
         if b <= 0 or name not in sq:
             continue
         cycles = sq[name] / N_SE
-        key = ("gemm_sparse32" if "gemm_sparse32" in name else
-               "gemm_dense32" if "gemm_dense32" in name else
-               "sparsify_kernel" if "sparsify_kernel" in name else
+        base = next((k for k in KERNEL_SOURCES if k in name), None)
+        inst = re.search(r"(gemm_sparse32|gemm_dense32|sparsify_kernel)<[^>]*>", name)
+        key = (inst.group(0).replace(" ", "") if inst is not None else base if base is not None else
                "torch.matmul (hipBLASLt " + name[:48] + ")" if "Cijk" in name else name[:60])
         kernels[key] = {"mfma_busy_cycles": round(b), "sq_busy_cycles": round(sq[name]),
                         "grbm_gui_active": round(grbm.get(name, 0.0)),
                         "kernel_cycles": round(cycles),
-                        "mfma_busy": round(b / (cycles * N_SIMD), 4)}
-    rec = {"workload": workload, "kernel_sha": source_sha(K2_SRC), "kernels": kernels,
+                        "mfma_busy": round(b / (cycles * N_SIMD), 4),
+                        "source_sha": source_sha(base) if base is not None else None}
+    rec = {"workload": workload, "kernels": kernels,
            "command": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE "
                       f"-d <dir> -o run -- python3 bench.py --steps 3 --warmup 1 --no-cpu --sets 1 "
                       f"--rounds 1 --calls 3 --workload {workload}"}
@@ -271,26 +360,83 @@ def summarize_mfma(sq_dir: str, workload: str) -> dict:
     return rec
 
 
-def mfma_busy_for(kernel_src: str, workload: str):
-    """Matrix-core busy fractions from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+def summarize_trace(trace_dir: str, workload: str, command: str) -> str:
+    """Per-kernel dispatch times (µs) and resources from a rocprofv3
+    --kernel-trace results database, as profiles/trace_<workload>.md."""
+    import collections
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(trace_dir, "**", "*_results.db"), recursive=True)
+    if len(dbs) != 1:
+        raise SystemExit(f"expected one results database under {trace_dir}, found {dbs}")
+    con = sqlite3.connect(dbs[0])
+    syms = {}
+    for kid, dem, kn, av, acv, sg, lds in con.execute(
+            "select id, demangled_kernel_name, kernel_name, arch_vgpr_count, accum_vgpr_count, "
+            "sgpr_count, group_segment_size from kernel_symbols"):
+        name = (dem or kn).replace("lynx::(anonymous namespace)::", "")
+        name = name[5:] if name.startswith("void ") else name
+        if not name.startswith("at::") and "(" in name:
+            name = name[:name.index("(")]
+        syms[kid] = (re.sub(r"\.kd$", "", name)[:70], av, acv, sg, lds)
+    times, wgs = collections.defaultdict(list), {}
+    for kid, t0, t1, gx, wx in con.execute(
+            "select kernel_id, start, end, grid_size_x, workgroup_size_x from rocpd_kernel_dispatch"):
+        times[kid].append((t1 - t0) / 1000.0)
+        wgs[kid] = gx // wx
+    con.close()
+    total = sum(sum(v) for v in times.values())
+    lines = [f"# Kernel trace: {workload} workload, bench.py", "",
+             "Command (on one MI355X, from the repository root, with `TMPDIR=/tmp`):", "", "```",
+             command, "```", "",
+             "Durations are per dispatch under the profiler (µs), from the run's results database, "
+             "over every call bench.py makes: the consecutive timed steps, then the interleaved "
+             "rounds of the sparse layer, the dense layer, the GEMM alone, the sparsifier alone "
+             "and torch.matmul (hipBLASLt).", "",
+             "| kernel | calls | avg µs | median µs | total µs | % of GPU time |",
+             "|---|---|---|---|---|---|"]
+    for kid, v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
+        med = sorted(v)[len(v) // 2]
+        lines.append(f"| `{syms[kid][0]}` | {len(v)} | {sum(v) / len(v):.1f} | {med:.1f} | "
+                     f"{sum(v):.0f} | {100 * sum(v) / total:.1f} |")
+    lines += ["", "Per-kernel dispatch statistics (µs) and resources:", "",
+              "| kernel | n | avg | min | max | arch VGPR | acc VGPR | SGPR | LDS B | workgroups |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for kid, v in sorted(times.items(), key=lambda kv: syms[kv[0]][0]):
+        n, av, acv, sg, lds = syms[kid]
+        lines.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
+                     f"{av} | {acv} | {sg} | {lds} | {wgs[kid]} |")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"trace_{workload}.md"), "w") as f:
+        f.write(text)
+    return text
+
+
+def mfma_busy_for(workload: str):
+    """Matrix-core busy fractions from the committed counter summary, for the
+    kernels whose sources are unchanged since it was taken (library kernels
+    always); None if there is no summary or nothing in it is current."""
     path = os.path.join(ROOT, "profiles", f"mfma_busy_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha") != source_sha(kernel_src):
-        return None
-    return {k: v["mfma_busy"] for k, v in rec["kernels"].items()}
+    out = {}
+    for k, v in rec.get("kernels", {}).items():
+        base = next((b for b in KERNEL_SOURCES if k.startswith(b)), None)
+        if base is None or v.get("source_sha") == source_sha(base):
+            out[k] = v["mfma_busy"]
+    return out or None
 
 
-def traffic_for(kernel_src: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def traffic_for(workload: str):
+    """HBM bytes per K2 launch from the committed rocprofv3 counter summary,
+    if it was taken on the current sources; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    return rec.get("bytes_per_launch") if rec.get("kernel_sha") == source_sha(kernel_src) else None
+    ok = rec.get("kernel_sha") == source_sha("gemm_sparse32")
+    return rec.get("bytes_per_step", rec.get("bytes_per_launch")) if ok else None
 
 
 def mfma_peak() -> dict:
@@ -332,6 +478,14 @@ def main():
         return
     if args.summarize_traffic:
         print(json.dumps(summarize_traffic(*args.summarize_traffic, args.workload)))
+        return
+    if args.cpu_table:
+        print(json.dumps(cpu_table()))
+        return
+    if args.summarize_trace:
+        cmd = (f"rocprofv3 --kernel-trace --stats -d <dir> -o run -- python3 bench.py "
+               f"--workload {args.workload} --steps {args.steps} --warmup {args.warmup} --no-cpu")
+        print(summarize_trace(args.summarize_trace, args.workload, cmd))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -434,7 +588,7 @@ def main():
     k2_alg_flops = sum(L.M * L.N * L.K + 2 * L.M * L.R * L.N
                        for L, sk in zip(layers, skipped) if not sk)
     k2_tflops = k2_alg_flops / (ms_gemm * 1e-3) / 1e12
-    traffic = traffic_for(K2_SRC, args.workload)
+    traffic = traffic_for(args.workload)
     # the sparsifier's algorithmic HBM bytes: read X and LB, write the packed
     # values and meta, s and T (2MK + 2RK + MK + MK/8 + 4M + 2MR per layer)
     k1_bytes = sum(2 * L.M * L.K + 2 * L.R * L.K + L.M * L.K + L.M * L.K // 8 + 4 * L.M
@@ -497,7 +651,7 @@ def main():
         # matrix-core busy fractions of the profiled kernels (rocprofv3
         # counters committed under profiles/, null once the kernel changed)
         "k2_hbm_gbps": None if traffic is None else round(traffic / (ms_gemm * 1e-3) / 1e9, 1),
-        "mfma_busy": mfma_busy_for(K2_SRC, args.workload),
+        "mfma_busy": mfma_busy_for(args.workload),
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec))

@@ -59,13 +59,13 @@ def test_traffic_scaled_by_the_copy_kernel(root):
     assert rec["write_bytes_per_launch"] == 500 * 1024
     assert rec["bytes_per_launch"] == 2000 * 1024 * 2 + 500 * 1024
     saved = json.load(open(root / "profiles" / "traffic_unit.json"))
-    assert saved["kernel_sha"] == bench.source_sha(bench.K2_SRC)
-    # the bench line uses it while the kernel source is unchanged ...
-    assert bench.traffic_for(bench.K2_SRC, "unit") == rec["bytes_per_launch"]
-    # ... and not once it was taken on another source
+    assert saved["kernel_sha"] == bench.source_sha("gemm_sparse32")
+    # the bench line uses it while the kernel's sources are unchanged ...
+    assert bench.traffic_for("unit") == rec["bytes_per_launch"]
+    # ... and not once it was taken on other sources
     saved["kernel_sha"] = "0" * 16
     json.dump(saved, open(root / "profiles" / "traffic_unit.json", "w"))
-    assert bench.traffic_for(bench.K2_SRC, "unit") is None
+    assert bench.traffic_for("unit") is None
 
 
 def test_traffic_needs_exactly_one_matching_kernel(root):
@@ -85,8 +85,39 @@ def test_mfma_busy_fraction(root):
         (K3, "SQ_VALU_MFMA_BUSY_CYCLES", 0.25 * kc * 1024), (K3, "SQ_BUSY_CYCLES", kc * 32),
         (COPY, "SQ_VALU_MFMA_BUSY_CYCLES", 0.0), (COPY, "SQ_BUSY_CYCLES", 5.0)])
     rec = bench.summarize_mfma(str(root / "s"), "unit")
-    assert rec["kernels"]["gemm_sparse32"]["mfma_busy"] == pytest.approx(0.5)
-    assert rec["kernels"]["gemm_sparse32"]["kernel_cycles"] == kc
-    assert rec["kernels"]["gemm_dense32"]["mfma_busy"] == pytest.approx(0.25)
+    assert rec["kernels"]["gemm_sparse32<4>"]["mfma_busy"] == pytest.approx(0.5)
+    assert rec["kernels"]["gemm_sparse32<4>"]["kernel_cycles"] == kc
+    assert rec["kernels"]["gemm_dense32<4>"]["mfma_busy"] == pytest.approx(0.25)
     assert not any("neg" in k for k in rec["kernels"])           # no matrix work: left out
-    assert bench.mfma_busy_for(bench.K2_SRC, "unit") == {"gemm_sparse32": 0.5, "gemm_dense32": 0.25}
+    assert bench.mfma_busy_for("unit") == {"gemm_sparse32<4>": 0.5, "gemm_dense32<4>": 0.25}
+    # a kernel whose sources changed since is dropped; the others stay
+    saved = json.load(open(root / "profiles" / "mfma_busy_unit.json"))
+    saved["kernels"]["gemm_dense32<4>"]["source_sha"] = "0" * 16
+    json.dump(saved, open(root / "profiles" / "mfma_busy_unit.json", "w"))
+    assert bench.mfma_busy_for("unit") == {"gemm_sparse32<4>": 0.5}
+
+
+def test_traffic_of_a_multi_layer_workload_is_per_step(root):
+    """The block launches K2 once per sparse layer (both tile widths): the
+    summary's per-step bytes are the mean per dispatch times the layers."""
+    mib = bench.COPY_MIB
+    K2n = K2.replace("<4>", "<3>")
+    make_db(str(root / "f"), [(COPY, "FETCH_SIZE", mib * 512.0), (K2, "FETCH_SIZE", 100.0),
+                              (K2n, "FETCH_SIZE", 300.0)])
+    make_db(str(root / "w"), [(COPY, "WRITE_SIZE", mib * 1024.0), (K2, "WRITE_SIZE", 10.0),
+                              (K2n, "WRITE_SIZE", 30.0)])
+    rec = bench.summarize_traffic(str(root / "f"), str(root / "w"), "block")
+    assert rec["launches_per_step"] == 4
+    assert rec["bytes_per_step"] == (200 * 2 + 20) * 1024 * 4
+    assert bench.traffic_for("block") == rec["bytes_per_step"]
+
+
+def test_source_hash_covers_the_kernel_headers(monkeypatch, tmp_path):
+    """Editing a header a kernel includes changes that kernel's hash."""
+    for name in ("k_gemm.hip", "lynx_tile.h", "lynx_dma.h", "lynx_internal.h"):
+        (tmp_path / name).write_text(name)
+    monkeypatch.setattr(bench, "CSRC", str(tmp_path))
+    before = bench.source_sha("gemm_sparse32")
+    (tmp_path / "lynx_tile.h").write_text("changed")
+    assert bench.source_sha("gemm_sparse32") != before
+    assert bench.source_sha("Cijk_library_kernel") is None
