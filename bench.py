@@ -70,6 +70,10 @@ def parse():
     p.add_argument("--summarize-trace", metavar="TRACE_DIR",
                    help="no GPU: write profiles/trace_<workload>.md from a rocprofv3 --kernel-trace "
                         "run of this benchmark and exit")
+    p.add_argument("--fusion-prototype", action="store_true",
+                   help="time the fused-sparsifier GEMM prototype (tests/proto) against the "
+                        "library's sparsifier + sparse GEMM pair on the MLP-up, MLP-down and QKV "
+                        "shapes (interleaved, --rounds x --calls) and exit")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into profiles/traffic_<workload>.json")
@@ -360,9 +364,20 @@ def summarize_mfma(sq_dir: str, workload: str) -> dict:
     return rec
 
 
-def summarize_trace(trace_dir: str, workload: str, command: str) -> str:
+TRACE_CALLS = ("over every call bench.py makes: the consecutive timed steps, then the "
+               "interleaved rounds of the sparse layer, the dense layer, the GEMM alone, the "
+               "sparsifier alone and torch.matmul (hipBLASLt).")
+FUSION_CALLS = ("over every call bench.py --fusion-prototype makes: per shape (MLP-up, "
+                "MLP-down, QKV), interleaved rounds of the library's layer (sparsifier + "
+                "sparse GEMM with the rank-64 LoRA), the sparsifier alone, the sparse GEMM alone "
+                "and the fused prototype (gemm_fused32: selection inside the GEMM's operand "
+                "load, no LoRA).")
+
+
+def summarize_trace(trace_dir: str, workload: str, command: str, calls: str = TRACE_CALLS,
+                    out_name: str | None = None) -> str:
     """Per-kernel dispatch times (µs) and resources from a rocprofv3
-    --kernel-trace results database, as profiles/trace_<workload>.md."""
+    --kernel-trace results database, as profiles/trace_<out_name or workload>.md."""
     import collections
     import glob
     import sqlite3
@@ -386,13 +401,12 @@ def summarize_trace(trace_dir: str, workload: str, command: str) -> str:
         wgs[kid] = gx // wx
     con.close()
     total = sum(sum(v) for v in times.values())
-    lines = [f"# Kernel trace: {workload} workload, bench.py", "",
+    title = f"{workload} workload, bench.py" if out_name is None else out_name.replace("_", " ")
+    lines = [f"# Kernel trace: {title}", "",
              "Command (on one MI355X, from the repository root, with `TMPDIR=/tmp`):", "", "```",
              command, "```", "",
              "Durations are per dispatch under the profiler (µs), from the run's results database, "
-             "over every call bench.py makes: the consecutive timed steps, then the interleaved "
-             "rounds of the sparse layer, the dense layer, the GEMM alone, the sparsifier alone "
-             "and torch.matmul (hipBLASLt).", "",
+             + calls, "",
              "| kernel | calls | avg µs | median µs | total µs | % of GPU time |",
              "|---|---|---|---|---|---|"]
     for kid, v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
@@ -407,7 +421,7 @@ def summarize_trace(trace_dir: str, workload: str, command: str) -> str:
         lines.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
                      f"{av} | {acv} | {sg} | {lds} | {wgs[kid]} |")
     text = "\n".join(lines) + "\n"
-    with open(os.path.join(ROOT, "profiles", f"trace_{workload}.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"trace_{out_name or workload}.md"), "w") as f:
         f.write(text)
     return text
 
@@ -468,6 +482,72 @@ def mfma_peak() -> dict:
     return out
 
 
+def fusion_prototype(rounds: int, calls: int, nsets: int) -> dict:
+    """The fused-sparsifier GEMM prototype against the library's pair: per
+    shape, the layer (sparsifier + sparse GEMM, rank-64 LoRA), each of its two
+    kernels alone and the prototype (no LoRA) take turns; medians in ms."""
+    import numpy as np
+    import torch
+
+    import activation_sparse_gemm_amd as lynx
+    from tests.proto import fused_proto
+    from workloads import make_config, make_layer
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(b):
+        return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    out = {}
+    for wl in ("mlp_up", "mlp_down", "qkv"):
+        base = make_config(wl)[0]
+        sets = []
+        for s in range(nsets):
+            L = base if s == 0 else make_layer(base.M, base.K, base.N, base.kind,
+                                               seed=100 + 10 * s, R=base.R, name=base.name)
+            d = dict(X=to_dev(L.X), W=to_dev(L.W), LA=to_dev(L.LA), LB=to_dev(L.LB))
+            d["Y"] = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
+            d["ws"] = torch.empty(lynx.workspace_bytes(L.M, L.K, L.R), dtype=torch.uint8,
+                                  device=dev)
+            d["packed"] = lynx.sparsify(d["X"], d["LB"])
+            sets.append(d)
+        S = len(sets)
+
+        def layer(i):
+            d = sets[i % S]
+            lynx.linear_sparse_lora(d["X"], d["W"], d["LA"], d["LB"], Y=d["Y"], workspace=d["ws"])
+
+        def sparsify(i):
+            d = sets[i % S]
+            v, m, sc, T = d["packed"]
+            lynx.sparsify(d["X"], d["LB"], out=dict(values=v, meta=m, scale=sc, T=T))
+
+        def gemm(i):
+            d = sets[i % S]
+            v, m, sc, T = d["packed"]
+            lynx.linear_sparse_lora_packed(v, m, sc, T, d["W"], d["LA"], Y=d["Y"])
+
+        def fused(i):
+            d = sets[i % S]
+            fused_proto.gemm_fused(d["X"], d["W"], Y=d["Y"])
+
+        fns = {"layer": layer, "sparsify": sparsify, "gemm": gemm, "fused": fused}
+        for fn in fns.values():
+            fn(0)
+        torch.cuda.synchronize()
+        med = time_interleaved(fns, rounds=rounds, calls=calls, stream=stream)
+        rec = {k: round(v[0], 5) for k, v in med.items()}
+        rec["fused_over_layer"] = round(med["fused"][0] / med["layer"][0], 3)
+        rec["fused_over_gemm"] = round(med["fused"][0] / med["gemm"][0], 3)
+        rec["shape"] = {"M": base.M, "K": base.K, "N": base.N, "R": base.R}
+        out[wl] = rec
+        print(f"fusion prototype {wl}: {rec}", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.synchronize()
+    return {"ms": out, "rounds": rounds, "calls": calls, "sets": nsets}
+
+
 def main():
     args = parse()
     if args.mfma_peak:
@@ -481,6 +561,15 @@ def main():
         return
     if args.cpu_table:
         print(json.dumps(cpu_table()))
+        return
+    if args.fusion_prototype:
+        if args.summarize_trace:
+            cmd = (f"rocprofv3 --kernel-trace --stats -d <dir> -o run -- python3 bench.py "
+                   f"--fusion-prototype --rounds {args.rounds} --calls {args.calls}")
+            print(summarize_trace(args.summarize_trace, "fusion", cmd, FUSION_CALLS,
+                                  out_name="fusion_prototype"))
+            return
+        print(json.dumps(fusion_prototype(args.rounds, args.calls, args.sets)))
         return
     if args.summarize_trace:
         cmd = (f"rocprofv3 --kernel-trace --stats -d <dir> -o run -- python3 bench.py "
