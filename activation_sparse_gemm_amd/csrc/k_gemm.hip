@@ -245,7 +245,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     constexpr int kPartA = kS - kBar - kR2 < kHalf ? kS - kBar - kR2 : kHalf;
     constexpr int kPartB = kHalf - kPartA;
     static_assert(kPartA > 0 && kPartB >= 0 && kR2 + kBar <= kS, "stage slots");
-    const int nk = K / 64;  // even: K is a multiple of 128
+    const int nk = K / 64;  // >= 2: the dispatcher sends K = 64 to the 64 x 64 kernel
     enum { kMain, kT, kLA, kNext0 };
     int m0 = 0, n0 = 0;
     // LoRA DMA instruction j (0..7) of wave w: LDS rows 8 (w + 4j) + l/8 of

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_dense32(const uint16_t* __restrict
     const int wm = wave & 1, wn = wave >> 1;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TN - 1) / TN;
     const int ntiles = tiles_m * tiles_n;
-    const int nk = K / 32;  // >= 4: K is a multiple of 128
+    const int nk = K / 32;  // >= 4: the dispatcher sends K = 64 to the 64 x 64 kernel
 
     // instruction j of wave w moves rows 16 (w + 4j) + l/4 of a 256-row operand
     // (64-byte LDS rows); lane l lands at byte 16 l of the instruction's 1 KB,

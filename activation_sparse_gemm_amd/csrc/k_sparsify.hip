@@ -9,9 +9,14 @@
 //
 // Work decomposition (one read of X):
 //   workgroup = ROWT row tiles of 16 rows (tokens) x all of K; its NW waves
-//   split K in 128-channel chunks.  Lane l: row r = l % 16 of every row tile,
-//   quarter q = l / 16; in chunk c it owns channels [128c + 32q, 128c + 32q + 32)
-//   of each of its ROWT rows: 8 groups of 4 per row, loaded as 4 x 16 bytes.
+//   split K in 128-channel chunks (the last one 64 channels wide when
+//   K % 128 == 64).  Lane l: row r = l % 16 of every row tile, quarter
+//   q = l / 16; in chunk c it owns channels [128c + 32q, 128c + 32q + 32) of
+//   each of its ROWT rows: 8 groups of 4 per row, loaded as 4 x 16 bytes.
+//   Lanes whose channels lie past K (quarters 2 and 3 of a 64-wide last chunk)
+//   load nothing, hold zeros (which add nothing to the norms or T) and store
+//   nothing; those checks are compiled only into the instantiation for
+//   K % 128 == 64 (HALF), so the loop for K % 128 == 0 carries none of them.
 //   - selection + packing in registers: 16 kept values (32 B) and 8 codes (4 B)
 //     per row, lane and chunk, stored in the 16-row x 64-channel tile order of
 //     the packed operand (a row tile is exactly one tile row-block; rows past M
@@ -94,8 +99,9 @@ __device__ __forceinline__ float dot2_self(uint32_t w, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(v, v, acc, false);
 }
 
-// RT = R / 16 column tiles of T (0..4); ROWT row tiles of 16 rows; NW waves
-template <int RT, int ROWT, int NW>
+// RT = R / 16 column tiles of T (0..4); ROWT row tiles of 16 rows; NW waves;
+// HALF: K % 128 == 64 (the last chunk is 64 channels wide)
+template <int RT, int ROWT, int NW, bool HALF>
 __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ LB, int M, int K,
     uint16_t* __restrict__ values, uint8_t* __restrict__ meta, float* __restrict__ scale,
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
     const int r = lane & 15;
     const int q = lane >> 4;
     const int m0 = blockIdx.x * kWgRows;
-    const int nchunks = K / kChunk;
+    const int nchunks = (K + kChunk - 1) / kChunk;
     const int steps = K / 64;
 
     const uint16_t* xrow[ROWT];
@@ -147,17 +153,23 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
 
     auto load_x = [&](int c, u32x4 (*xd)[4]) {
         const int k = c * kChunk + q * 32;
+        // K % 64 == 0: a lane's 32 channels are all in range or all past K
+        const bool live = !HALF || k < K;
 #pragma unroll
         for (int u = 0; u < ROWT; ++u)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xd[u][i] = *reinterpret_cast<const u32x4*>(xrow[u] + k + 8 * i);
+            for (int i = 0; i < 4; ++i)
+                xd[u][i] = live ? *reinterpret_cast<const u32x4*>(xrow[u] + k + 8 * i)
+                                : u32x4{0u, 0u, 0u, 0u};
     };
     auto load_lb = [&](int c, u32x4* ld) {
+        const int k = c * kChunk + 8 * (lane & 15);
+        const bool live = !HALF || k < K;
 #pragma unroll
         for (int j = 0; j < (RT > 0 ? R / 4 : 0); ++j) {
             const int lr = 4 * j + (lane >> 4);
-            ld[j] = *reinterpret_cast<const u32x4*>(LB + size_t(lr) * size_t(K) +
-                                                    size_t(c) * kChunk + 8 * (lane & 15));
+            ld[j] = live ? *reinterpret_cast<const u32x4*>(LB + size_t(lr) * size_t(K) + k)
+                         : u32x4{0u, 0u, 0u, 0u};
         }
     };
     u32x4 xv[ROWT][4], lbraw[RT > 0 ? R / 4 : 1];
@@ -199,7 +211,9 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
             const int step = k >> 6, half = q & 1;
             u32x4* vdst = reinterpret_cast<u32x4*>(vtile + (size_t(u) * steps + step) * 512 + half * 16);
             uint32_t* mdst = reinterpret_cast<uint32_t*>(mtile + (size_t(u) * steps + step) * 128 + half * 4);
-            if (row_ok[u]) {
+            if (HALF && k >= K) {
+                // channels past K (64-wide last chunk): nothing to store
+            } else if (row_ok[u]) {
                 vdst[0] = u32x4{kept[0], kept[1], kept[2], kept[3]};
                 vdst[1] = u32x4{kept[4], kept[5], kept[6], kept[7]};
                 *mdst = code;
@@ -324,20 +338,30 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
 // R = 64 (µs, K = 3072 / 12288: 16.3 / 52.4, 24.0 / 75.0, 29.7 / 92.1).
 constexpr float kRowtCost[4] = {0.f, 1.0f, 1.45f, 1.8f};
 
-template <int RT>
+template <int RT, bool HALF>
 void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uint16_t* LB,
                uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, hipStream_t stream) {
     const int nw = rowt == 1 ? 8 : 4;
     const dim3 grid((M + kRows * rowt - 1) / (kRows * rowt)), block(64 * (nchunks < nw ? nchunks : nw));
     if (rowt == 1) {
-        hipLaunchKernelGGL((sparsify_kernel<RT, 1, 8>), grid, block, 0, stream, X, LB, M, K, values,
-                           meta, scale, T);
+        hipLaunchKernelGGL((sparsify_kernel<RT, 1, 8, HALF>), grid, block, 0, stream, X, LB, M, K,
+                           values, meta, scale, T);
     } else if (rowt == 2) {
-        hipLaunchKernelGGL((sparsify_kernel<RT, 2, 4>), grid, block, 0, stream, X, LB, M, K, values,
-                           meta, scale, T);
+        hipLaunchKernelGGL((sparsify_kernel<RT, 2, 4, HALF>), grid, block, 0, stream, X, LB, M, K,
+                           values, meta, scale, T);
     } else {
-        hipLaunchKernelGGL((sparsify_kernel<RT, 3, 4>), grid, block, 0, stream, X, LB, M, K, values,
-                           meta, scale, T);
+        hipLaunchKernelGGL((sparsify_kernel<RT, 3, 4, HALF>), grid, block, 0, stream, X, LB, M, K,
+                           values, meta, scale, T);
+    }
+}
+
+template <int RT>
+void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uint16_t* LB,
+               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, hipStream_t stream) {
+    if (K % kChunk == 0) {
+        launch_rt<RT, false>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
+    } else {
+        launch_rt<RT, true>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
     }
 }
 
@@ -346,7 +370,7 @@ void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uin
 lynx_status launch_sparsify(const uint16_t* X, const uint16_t* LB, int M, int K, int R,
                             uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,
                             hipStream_t stream) {
-    const int nchunks = K / kChunk;
+    const int nchunks = (K + kChunk - 1) / kChunk;
     // Row tiles per workgroup: the fewest rounds of workgroups over the compute
     // units, weighted by the measured cost of a workgroup (one tile when there
     // is no LoRA: nothing is shared between row tiles then).

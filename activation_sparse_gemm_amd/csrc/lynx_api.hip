@@ -29,7 +29,7 @@ bool rank_ok(int64_t R) { return R == 0 || R == 16 || R == 32 || R == 48 || R ==
 bool dims_ok(int64_t M, int64_t N, int64_t K) {
     if (M < 0 || N < 0 || K <= 0) return false;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return false;
-    if (K % 128 != 0) return false;
+    if (K % 64 != 0) return false;
     if ((M + kPad) * K >= kMaxElems || (N + kPad) * K >= kMaxElems || (M + kPad) * N >= kMaxElems)
         return false;
     return true;

@@ -30,7 +30,7 @@
  *   - Asynchronous device faults surface at the caller's next synchronization
  *     with the stream, not as a status of the call that queued the work.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs.
- *   - Shape limits: K is a positive multiple of 128; M >= 0 and N >= 0 (0 is a
+ *   - Shape limits: K is a positive multiple of 64; M >= 0 and N >= 0 (0 is a
  *     no-op); R (LoRA rank) is one of 0, 16, 32, 48, 64 (0 = no LoRA branch);
  *     M, N, K <= 2^24; (M + 256) * K, (N + 256) * K and (M + 256) * N are each
  *     below 2^31 (every tensor, padded by one 256-row tile, smaller than 2^31

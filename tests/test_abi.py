@@ -55,7 +55,10 @@ def test_workspace_bytes():
     assert ws == 4096 * 3072 + 4096 * 3072 // 8 + 4096 * 4 + 4096 * 64 * 2
     # M = 3 -> 16 stored rows: values 16*128 B, meta 16*16 B, scale and T rounded to 256 B
     assert _abi.workspace_bytes(3, 128, 16) == 2048 + 256 + 256 + 256
-    assert _abi.workspace_bytes(16, 100, 0) == 0      # K not a multiple of 128
+    assert _abi.workspace_bytes(16, 100, 0) == 0      # K not a multiple of 64
+    assert _abi.workspace_bytes(16, 96, 0) == 0
+    assert _abi.workspace_bytes(16, 64, 0) > 0       # K % 64 == 0 is enough
+    assert _abi.workspace_bytes(16, 192, 16) > 0
     assert _abi.workspace_bytes(16, 128, 8) == 0      # unsupported rank
     assert _abi.workspace_bytes(-1, 128, 0) == 0
 
@@ -65,7 +68,7 @@ def call_sparsify(X=A, LB=A, M=16, K=128, R=16, values=A, meta=A, scale=A, T=A):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(K=64), SHAPE), (dict(M=-1), SHAPE),
+    (dict(K=100), SHAPE), (dict(K=0), SHAPE), (dict(K=96), SHAPE), (dict(M=-1), SHAPE),
     (dict(R=8), SHAPE), (dict(R=80), SHAPE), (dict(M=1 << 25), SHAPE),
     (dict(X=None), NULL), (dict(values=None), NULL), (dict(meta=None), NULL),
     (dict(scale=None), NULL), (dict(LB=None), NULL), (dict(T=None), NULL),
@@ -81,7 +84,7 @@ def call_linear(X=A, W=A, LA=A, LB=A, Y=A, M=16, N=16, K=128, R=16, ws=B, wsb=1 
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=192), SHAPE), (dict(N=-3), SHAPE), (dict(R=17), SHAPE),
+    (dict(K=160), SHAPE), (dict(N=-3), SHAPE), (dict(R=17), SHAPE),
     (dict(W=None), NULL), (dict(LA=None), NULL), (dict(Y=None), NULL),
     (dict(Y=A + 2), ALIGN), (dict(ws=B + 16), ALIGN),
     (dict(ws=None), WORKSPACE), (dict(wsb=100), WORKSPACE),
@@ -101,7 +104,7 @@ def call_noalloc(X=A, W=A, LA=A, LB=A, Y=A, M=16, N=16, K=128, R=16):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=192), SHAPE), (dict(R=17), SHAPE), (dict(M=1 << 25), SHAPE),
+    (dict(K=160), SHAPE), (dict(R=17), SHAPE), (dict(M=1 << 25), SHAPE),
     (dict(W=None), NULL), (dict(LB=None), NULL), (dict(Y=A + 2), ALIGN),
     (dict(M=0), OK), (dict(N=0), OK),
     # the static scratch array holds LYNX_SCRATCH_BYTES = 64 MiB
@@ -145,6 +148,22 @@ def test_packed_validation(kw, status):
 ])
 def test_dense_validation(args, status):
     assert _abi.lib().lynx_linear_dense(*args, None) == status
+
+
+@pytest.mark.parametrize("K,ok", [(32, False), (96, False), (160, False), (64, True), (192, True),
+                                  (320, True)])
+def test_k_must_be_a_multiple_of_64(K, ok):
+    """K % 64 == 0 passes validation (without a GPU the call then stops at the
+    device check); anything else is LYNX_ERR_SHAPE for every entry point."""
+    import torch
+    if ok and torch.cuda.is_available():
+        pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
+    want = UNSUPPORTED if ok else SHAPE
+    assert call_linear(K=K) == want
+    assert call_packed(K=K) == want
+    assert call_sparsify(K=K) == want
+    assert call_noalloc(K=K) == want
+    assert _abi.lib().lynx_linear_dense(A, A, A, 16, 16, K, None) == want
 
 
 # The tiled kernels address every operand with unsigned 32-bit byte offsets,
