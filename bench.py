@@ -375,7 +375,7 @@ FUSION_CALLS = ("over every call bench.py --fusion-prototype makes: per shape (M
 
 
 def summarize_trace(trace_dir: str, workload: str, command: str, calls: str = TRACE_CALLS,
-                    out_name: str | None = None) -> str:
+                    out_name: str | None = None, timeline: int = 0) -> str:
     """Per-kernel dispatch times (µs) and resources from a rocprofv3
     --kernel-trace results database, as profiles/trace_<out_name or workload>.md."""
     import collections
@@ -395,10 +395,13 @@ def summarize_trace(trace_dir: str, workload: str, command: str, calls: str = TR
             name = name[:name.index("(")]
         syms[kid] = (re.sub(r"\.kd$", "", name)[:70], av, acv, sg, lds)
     times, wgs = collections.defaultdict(list), {}
+    order = []
     for kid, t0, t1, gx, wx in con.execute(
-            "select kernel_id, start, end, grid_size_x, workgroup_size_x from rocpd_kernel_dispatch"):
+            "select kernel_id, start, end, grid_size_x, workgroup_size_x from rocpd_kernel_dispatch "
+            "order by start"):
         times[kid].append((t1 - t0) / 1000.0)
         wgs[kid] = gx // wx
+        order.append((kid, (t1 - t0) / 1000.0))
     con.close()
     total = sum(sum(v) for v in times.values())
     title = f"{workload} workload, bench.py" if out_name is None else out_name.replace("_", " ")
@@ -420,6 +423,15 @@ def summarize_trace(trace_dir: str, workload: str, command: str, calls: str = TR
         n, av, acv, sg, lds = syms[kid]
         lines.append(f"| `{n}` | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} | {max(v):.1f} | "
                      f"{av} | {acv} | {sg} | {lds} | {wgs[kid]} |")
+    if timeline:
+        # from the sparsifier launch before the first sparse GEMM (the first
+        # step; bench.py's set-up calls only the sparsifier before it)
+        first = next((i for i, (kid, _) in enumerate(order) if "gemm_sparse32" in syms[kid][0]), 1)
+        first = max(first - 1, 0)
+        lines += ["", f"{timeline} dispatches in time order from the first step (µs):", "",
+                  "| # | kernel | µs |", "|---|---|---|"]
+        lines += [f"| {i} | `{syms[kid][0]}` | {d:.1f} |"
+                  for i, (kid, d) in enumerate(order[first:first + timeline], start=first)]
     text = "\n".join(lines) + "\n"
     with open(os.path.join(ROOT, "profiles", f"trace_{out_name or workload}.md"), "w") as f:
         f.write(text)
@@ -508,7 +520,7 @@ def fusion_prototype(rounds: int, calls: int, nsets: int) -> dict:
                                                seed=100 + 10 * s, R=base.R, name=base.name)
             d = dict(X=to_dev(L.X), W=to_dev(L.W), LA=to_dev(L.LA), LB=to_dev(L.LB))
             d["Y"] = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
-            d["ws"] = torch.empty(lynx.workspace_bytes(L.M, L.K, L.R), dtype=torch.uint8,
+            d["ws"] = torch.empty(lynx.workspace_bytes(L.M, L.N, L.K, L.R), dtype=torch.uint8,
                                   device=dev)
             d["packed"] = lynx.sparsify(d["X"], d["LB"])
             sets.append(d)
@@ -611,7 +623,7 @@ def main():
                                                seed=100 + 10 * s + j, R=base.R, name=base.name)
             X, W, LA, LB = to_dev(L.X), to_dev(L.W), to_dev(L.LA), to_dev(L.LB)
             M, K, N, R = L.M, L.K, L.N, L.R
-            ws = torch.empty(lynx.workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
+            ws = torch.empty(lynx.workspace_bytes(M, N, K, R), dtype=torch.uint8, device=dev)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             packed = lynx.sparsify(X, LB)
