@@ -21,7 +21,7 @@ STATUS_NAMES = {
     4: "LYNX_ERR_WORKSPACE", 5: "LYNX_ERR_DEVICE", 6: "LYNX_ERR_UNSUPPORTED_DEVICE",
     7: "LYNX_ERR_SCRATCH",
 }
-SCRATCH_BYTES = 128 << 20  # LYNX_SCRATCH_BYTES
+SCRATCH_BYTES = 64 << 20  # LYNX_SCRATCH_BYTES
 
 LAYER_SPARSE_LORA, LAYER_DENSE = 0, 1
 
@@ -40,7 +40,7 @@ _LP = ctypes.POINTER(Layer)
 SIGNATURES = {
     "lynx_status_string": (ctypes.c_char_p, [_I]),
     "lynx_version": (_I, []),
-    "lynx_workspace_bytes": (_SZ, [_I64, _I64, _I64, _I64]),
+    "lynx_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "lynx_sparsify": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "lynx_linear_sparse_lora": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _SZ, _P]),
     "lynx_linear_sparse_lora_packed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
@@ -51,9 +51,6 @@ SIGNATURES = {
     "lynx_linear_sequence": (_I, [_LP, _I64, _P, _SZ, _P]),
     "lynx_probe_mfma": (_I, [_I, _I, _P, _P, _P, _P, _P]),
     "lynx_probe_mfma_rate": (_I, [_I, _I, _I, _P, _P, _P]),
-    "lynx_probe_sparse_plan": (_I, [_I64, _I64, _I64, ctypes.c_int32, ctypes.c_int32, _P]),
-    "lynx_probe_gemm_sparse_ws": (_I, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P,
-                                       _SZ, _P]),
 }
 
 
@@ -114,10 +111,8 @@ def version() -> int:
     return lib().lynx_version()
 
 
-def workspace_bytes(M: int, N: int, K: int, R: int) -> int:
-    """Workspace of lynx_linear_sparse_lora for an (M, N, K, R) problem on the
-    current device (include/lynx.h)."""
-    return lib().lynx_workspace_bytes(M, N, K, R)
+def workspace_bytes(M: int, K: int, R: int) -> int:
+    return lib().lynx_workspace_bytes(M, K, R)
 
 
 def padded_rows(M: int) -> int:
@@ -176,7 +171,7 @@ def linear_sparse_lora(X, W, LA=None, LB=None, Y=None, workspace=None):
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
     _need(Y, torch.bfloat16, (M, N), "Y")
-    nbytes = workspace_bytes(M, N, K, R)
+    nbytes = workspace_bytes(M, K, R)
     if workspace is None:
         workspace = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=X.device)
     _check(lib().lynx_linear_sparse_lora(_ptr(X), _ptr(W), _ptr(LA), _ptr(LB), _ptr(Y), M, N, K,
@@ -229,46 +224,6 @@ def linear_sparse_lora_packed(values, meta, scale, T, W, LA=None, Y=None):
                                                 _stream(W.device)),
            "lynx_linear_sparse_lora_packed")
     return Y
-
-
-def linear_sparse_lora_packed_ws(values, meta, scale, T, W, LA, workspace, Y=None):
-    """The sparse GEMM alone with the layer's schedule, stream-K included
-    (lynx_probe_gemm_sparse_ws, a test hook); same operands as
-    linear_sparse_lora_packed plus a workspace for the partial sums."""
-    M = scale.shape[0]
-    N, K = W.shape
-    Mp = padded_rows(M)
-    R = 0 if LA is None else LA.shape[1]
-    _need(values, torch.bfloat16, (Mp * K // 2,), "values")
-    _need(meta, torch.uint8, (Mp * K // 8,), "meta")
-    _need(scale, torch.float32, (M,), "scale")
-    _need(W, torch.bfloat16, (N, K), "W")
-    if R > 0:
-        _need(T, torch.bfloat16, (M, R), "T")
-        _need(LA, torch.bfloat16, (N, R), "LA")
-    if Y is None:
-        Y = torch.empty((M, N), dtype=torch.bfloat16, device=W.device)
-    _need(Y, torch.bfloat16, (M, N), "Y")
-    _check(lib().lynx_probe_gemm_sparse_ws(_ptr(values), _ptr(meta), _ptr(scale),
-                                           _ptr(T) if R > 0 else None, _ptr(W),
-                                           _ptr(LA) if R > 0 else None, _ptr(Y), M, N, K, R,
-                                           _ptr(workspace), workspace.numel(),
-                                           _stream(W.device)),
-           "lynx_probe_gemm_sparse_ws")
-    return Y
-
-
-PLAN_FIELDS = ("tiled", "width", "grid", "dp_tiles", "sk_tiles", "pairs", "partial_bytes",
-               "flag_bytes")
-
-
-def sparse_plan(M: int, N: int, K: int, with_sk: bool = True, cus: int = 256) -> dict:
-    """The sparse GEMM's schedule for a device of `cus` compute units
-    (lynx_probe_sparse_plan, host only)."""
-    out = (ctypes.c_int64 * 8)()
-    _check(lib().lynx_probe_sparse_plan(M, N, K, 1 if with_sk else 0, cus, out),
-           "lynx_probe_sparse_plan")
-    return dict(zip(PLAN_FIELDS, (int(v) for v in out)))
 
 
 def linear_dense(X, W, Y=None):

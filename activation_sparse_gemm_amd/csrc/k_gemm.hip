@@ -61,20 +61,6 @@ struct Cfg {
     static_assert(2 * DMA_PER_STAGE < 64, "vmcnt range");
 };
 
-// Stream-K arguments of K2 (all zero for whole tiles only).
-struct SkArgs {
-    float* partials;  // one slot of raw accumulators per range (64 KB x NB)
-    int* flags;       // per stream-K tile: partial sums handed in (zero at launch)
-    int dp_tiles;     // whole tiles: tile-order indices [0, dp_tiles)
-    int sk_tiles;     // stream-K tiles: indices [dp_tiles, dp_tiles + sk_tiles)
-    int pairs;        // stage pairs of the stream-K tiles, sk_tiles * K / 128 (>= grid)
-};
-// role of a unit of work
-enum { kWhole = 0, kOwner = 1, kPartial = 2 };
-// an owner's wait for the partial sums: at most this many polls ~128 cycles
-// apart (about a quarter of a second), then it goes on
-constexpr int kSpinLimit = 1 << 21;
-
 // ---------------------------------------------------------------------------
 // K2: Y = s * (X~ W^T) + T LA^T with v_smfmac_f32_32x32x32_bf16.
 //
@@ -98,7 +84,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const uint16_t* __restrict__ values, const uint8_t* __restrict__ meta,
     const float* __restrict__ scale, const uint16_t* __restrict__ T,
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ LA,
-    uint16_t* __restrict__ Y, int M, int N, int K, int R, const SkArgs sk) {
+    uint16_t* __restrict__ Y, int M, int N, int K, int R) {
     using C = Cfg<NB>;
     constexpr int TN = C::TILE_N;   // tile columns
     constexpr int WC = 32 * NB;     // columns per wave
@@ -116,6 +102,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const int wm = wave & 1, wn = wave >> 1;
 
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + TN - 1) / TN;
+    const int ntiles = tiles_m * tiles_n;
 
     // ---- DMA addressing ----------------------------------------------------
     // values: instruction j of wave w moves the 1 KB value tile of row block
@@ -136,28 +123,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const i32x4 rsL = make_rsrc(LA, uint32_t(N) * uint32_t(2 * R));
     const i32x4 rsS = make_rsrc(scale, uint32_t(M) * 4u);
     uint32_t voffA[C::A_DMA], voffB[C::B_DMA], voffM[C::M_DMA];
-    // offsets of the tile at (tm0, tn0) from its 64-channel stage kb on
-    // (stage t of the unit then adds t to kb through the DMA's scalar offset)
-    auto set_tile_offsets = [&](int tm0, int tn0, int kb) {
+    auto set_tile_offsets = [&](int tm0, int tn0) {
 #pragma unroll
         for (int j = 0; j < C::A_DMA; ++j) {
             const int blk = wave + 4 * j, row = lane >> 2, ph = lane & 3;
-            voffA[j] = (uint32_t(tm0 / 16 + blk) * uint32_t(steps) + uint32_t(kb)) * 1024u +
-                       uint32_t(row * 64 + 16 * (ph ^ swz64(row)));
+            voffA[j] = uint32_t(tm0 / 16 + blk) * uint32_t(steps) * 1024u + uint32_t(row * 64 + 16 * (ph ^ swz64(row)));
         }
 #pragma unroll
         for (int j = 0; j < C::B_DMA; ++j) {
             const int row = 8 * (wave + 4 * j) + (lane >> 3), ph = lane & 7;
-            voffB[j] = uint32_t(tn0 + row) * uint32_t(2 * K) + uint32_t(kb) * 128u +
-                       uint32_t(16 * (ph ^ swz128(row)));
+            voffB[j] = uint32_t(tn0 + row) * uint32_t(2 * K) + uint32_t(16 * (ph ^ swz128(row)));
         }
 #pragma unroll
         for (int j = 0; j < C::M_DMA; ++j) {
             // rows 16..31 of each 32-row group (lanes 32..63) land with their
             // two dwords swapped, so a fragment's 32 rows read 32 banks
             const int blk = 2 * (wave + 4 * j) + (lane >> 5);
-            voffM[j] = (uint32_t(tm0 / 16 + blk) * uint32_t(steps) + uint32_t(kb)) * 128u +
-                       uint32_t(4 * ((lane & 31) ^ (lane >> 5)));
+            voffM[j] = uint32_t(tm0 / 16 + blk) * uint32_t(steps) * 128u + uint32_t(4 * ((lane & 31) ^ (lane >> 5)));
         }
     };
     // one of the DMA instructions of a stage (4 value tiles, 2 meta, 2 NB W)
@@ -264,8 +246,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     constexpr int kPartB = kHalf - kPartA;
     static_assert(kPartA > 0 && kPartB >= 0 && kR2 + kBar <= kS, "stage slots");
     const int nk = K / 64;  // >= 2: the dispatcher sends K = 64 to the 64 x 64 kernel
-    // stages of the current unit (a whole tile: nk; a stream-K segment: fewer, >= 2)
-    int klen = nk;
     enum { kMain, kT, kLA, kNext0 };
     int m0 = 0, n0 = 0;
     // LoRA DMA instruction j (0..7) of wave w: LDS rows 8 (w + 4j) + l/8 of
@@ -378,80 +358,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
     const float* s_lds = reinterpret_cast<const float*>(smem + C::SCALE_OFF);
     char* ep = smem + kEpiOff + wave * kEpiWave;
 
-    // ---- work units: this workgroup's stream-K segments, then its whole tiles.
-    // Whole tiles are tile-order indices bid = blockIdx.x + i * gridDim.x
-    // below sk.dp_tiles.  The stream-K tiles are the indices sk.dp_tiles ..
-    // + sk.sk_tiles - 1; their 64-channel stages, counted in pairs, are split
-    // into gridDim.x contiguous ranges, range rho = floor(rho * pairs / P) ..
-    // floor((rho + 1) * pairs / P) - 1, numbered XCD-major (workgroup w runs
-    // on XCD w % 8), so that the few ranges meeting in a tile share an L2.
-    // A range is shorter than a tile (sk_tiles < P): it is at most two
-    // segments, the end of one tile and the start of the next.  The segment
-    // that holds a tile's stage 0 owns the tile: it waits for the others'
-    // partial sums, adds them in range order and finishes the tile.  Every
-    // other segment is the first unit of its workgroup, so no segment that
-    // others wait for waits itself.
-    const int P = gridDim.x;
-    const int rho = sk.sk_tiles > 0 && (P & 7) == 0 ? (blockIdx.x & 7) * (P >> 3) + (blockIdx.x >> 3)
-                                                    : int(blockIdx.x);
-    // the range that holds stage pair p of the stream-K tiles
-    auto range_of_pair = [&](int p) {
-        return int((int64_t(p + 1) * P + sk.pairs - 1) / sk.pairs) - 1;
-    };
-    // this range's stages [sk_s0, sk_s1) of the stream-K tiles, nseg segments
-    int sk_s0 = 0, sk_s1 = 0, nseg = 0;
-    if (sk.sk_tiles > 0) {
-        sk_s0 = int(2 * (int64_t(rho) * sk.pairs / P));
-        sk_s1 = int(2 * (int64_t(rho + 1) * sk.pairs / P));
-        if (sk_s1 > sk_s0) nseg = (sk_s1 - 1) / nk - sk_s0 / nk + 1;
-    }
-    // unit u: its tile-order index, first stage, stage count and role
-    auto unit = [&](int u, int& bid, int& kb, int& len, int& role) {
-        if (u < nseg) {
-            const int t = sk_s0 / nk + u;
-            const int s = max(sk_s0, t * nk), e = min(sk_s1, (t + 1) * nk);
-            bid = sk.dp_tiles + t;
-            kb = s - t * nk;
-            len = e - s;
-            role = kb != 0 ? kPartial : (len == nk ? kWhole : kOwner);
-            return true;
-        }
-        bid = int(blockIdx.x) + (u - nseg) * P;
-        kb = 0;
-        len = nk;
-        role = kWhole;
-        return bid < sk.dp_tiles;
-    };
-
-    // the output tile of tile index bid
-    auto tile_coords = [&](int b, int& tm, int& tn) {
-        if (b < sk.dp_tiles) {
-            tile_of(b, tiles_m, tiles_n, tm, tn);
-        } else {
-            tile_at(sk_tile_position(b - sk.dp_tiles, tiles_m * tiles_n, sk.dp_tiles), tiles_m,
-                    tiles_n, tm, tn);
-        }
-    };
-    int u = 0, bid = 0, kb0 = 0, role = kWhole;
-    bool valid = unit(0, bid, kb0, klen, role);
-    if (valid) {
+    int v = blockIdx.x;
+    {
         int tm, tn;
-        tile_coords(bid, tm, tn);
+        tile_of(v, tiles_m, tiles_n, tm, tn);
         m0 = tm * BM;
         n0 = tn * TN;
-        set_tile_offsets(m0, n0, kb0);
-        __builtin_amdgcn_s_waitcnt(0);
-        for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, uint32_t(cur), k);  // first unit's stage 0
     }
+    set_tile_offsets(m0, n0);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(0, uint32_t(cur), k);  // first tile's stage 0
 
-    while (valid) {
-        // stage 0 of this unit is in flight into slot `cur`
+    for (; v < ntiles; v += gridDim.x) {
+        // stage 0 of this tile is in flight into slot `cur`
 #pragma unroll
         for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[a][b] = f32x16{};
         for (int k = 0; k < C::DMA_PER_STAGE; ++k) dma_k(1, uint32_t(nxt), k);
-        if (klen > 2) {
+        if (nk > 2) {
             for (int i = 0; i < kPartA; ++i) dma_grp(IMain{}, 2, aft, 0, i);
             wait_vmcnt<C::DMA_PER_STAGE + kPartA>();  // stage 0 has landed
         } else {
@@ -470,22 +395,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 #pragma unroll
         for (int n = 0; n < kReads; ++n) read_n(cur, 0, fr[0], n);
 
-        for (int t = 0; t < klen - 3; ++t) stage(t, IMain{}, IMain{});
-        if (klen >= 3) stage(klen - 3, IMain{}, IT{});
-        stage(klen - 2, IT{}, ILA{});
-        // the current unit's stage loads are all issued: point the offsets at
-        // the next unit, whose stage 0 goes out from here on
-        int nbid = 0, nkb = 0, nlen = nk, nrole = kWhole;
-        has_next = unit(u + 1, nbid, nkb, nlen, nrole);
+        for (int t = 0; t < nk - 3; ++t) stage(t, IMain{}, IMain{});
+        if (nk >= 3) stage(nk - 3, IMain{}, IT{});
+        stage(nk - 2, IT{}, ILA{});
+        // the current tile's stage loads are all issued: point the offsets at
+        // the next tile, whose stage 0 goes out from here on
+        const int vn = v + gridDim.x;
+        has_next = vn < ntiles;
         int m0n = m0, n0n = n0;
         if (has_next) {
             int tm, tn;
-            tile_coords(nbid, tm, tn);
+            tile_of(vn, tiles_m, tiles_n, tm, tn);
             m0n = tm * BM;
             n0n = tn * TN;
-            set_tile_offsets(m0n, n0n, nkb);
+            set_tile_offsets(m0n, n0n);
         }
-        stage(klen - 1, ILA{}, INext0{});
+        stage(nk - 1, ILA{}, INext0{});
         // rotation after the last stage: cur = T, nxt = LA, aft = next stage 0
         for (int i = kPartA; i < kHalf; ++i) dma_grp(INext0{}, 0, aft, 0, i);
         for (int i = 0; i < kHalf; ++i) dma_grp(INext0{}, 0, aft, 1, i);
@@ -496,220 +421,127 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
         }
         __syncthreads();  // LoRA operands landed; all waves done with the stage slots
 
-        // stream-K: range r's slot holds its raw accumulators, wave by wave,
-        // as 1 KB rows (64 lanes x 16 bytes) in (a, b, group-of-4) order.  The
-        // slots and flags are written and read with device-scope accesses
-        // (sc1: coherent across the XCDs' L2s without writing back or
-        // invalidating either cache, which would cost every other workgroup
-        // on the XCD its cached operands).  A hand-over is: the slot's stores,
-        // each wave waiting until they are done, a barrier, then one
-        // device-scope add to the tile's flag; the owner polls the flag with
-        // device-scope loads, then reads the slots with device-scope loads.
-        // 4 waves x 4 x NB accumulator tiles x 4 groups of 4 x 64 lanes x 16 B
-        constexpr int kSlotBytes = 4 * 4 * NB * 4 * 64 * 16;
-        static_assert(kSlotBytes == 65536 * NB, "the host plan's slot size");
-        constexpr int kCpolDevice = 16;                            // sc1
-        auto slot_off = [&](int r, int a, int b, int g) {
-            return uint32_t(r) * uint32_t(kSlotBytes) +
-                   uint32_t((((wave * 4 + a) * NB + b) * 4 + g) * 64 + fresh_lane()) * 16u;
-        };
-        if (role == kPartial) {
-            // a range's first segment, inside a tile it does not own: hand the
-            // partial sum to the tile's owner
-            const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
-                sk.partials, 0, int(uint32_t(gridDim.x) * uint32_t(kSlotBytes)), kRsrcWord3);
+        // ---- y = s * acc + T LA^T: rows scaled by s, then the LoRA up-projection
+        // accumulated on top, with T as stored (no bf16 rounding of T / s)
 #pragma unroll
-            for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + wm * 128 + 32 * a + 8 * j + 4 * h);
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
-                    for (int g = 0; g < 4; ++g)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4, f32x4{acc[a][b][4 * g], acc[a][b][4 * g + 1],
-                                                            acc[a][b][4 * g + 2],
-                                                            acc[a][b][4 * g + 3]}),
-                            rsP, slot_off(rho, a, b, g), 0, kCpolDevice);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int i = 0; i < 4; ++i) acc[a][b][4 * j + i] *= sv[i];
             }
-            // this wave's stores are complete (at the device's coherence
-            // point, sc1) before the barrier; then the flag
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            if (tid == 0)
-                __hip_atomic_fetch_add(sk.flags + (bid - sk.dp_tiles), 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            if (role == kOwner) {
-                // wait for the tile's other ranges (rho + 1 .. last), then add their
-                // partial sums in range order
-                const int t = bid - sk.dp_tiles;
-                const int last = range_of_pair((t + 1) * (nk >> 1) - 1);
-                if (tid == 0) {
-                    // bounded: every awaited segment is the first unit of its
-                    // workgroup and never waits itself, so the count arrives
-                    for (int it = 0; it < kSpinLimit; ++it) {
-                        if (__hip_atomic_load(sk.flags + t, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) >= last - rho)
-                            break;
-                        __builtin_amdgcn_s_sleep(2);
-                    }
+        if (R > 0) {
+            const char* Ts = smem + cur;
+            const char* Ls = smem + nxt;
+            // T is dense; it is fed to the same SMFMAC as two exactly-2:4
+            // halves with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per
+            // group): over channels [16h, 16h+16) of a 32-rank step the even
+            // dwords of the row are positions 0,1 of each group and the odd
+            // dwords positions 2,3.  LA supplies the B operand exactly as W
+            // does in the main loop.
+            const int nks = (R + 31) / 32;  // 1 or 2 (R <= 64)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks >= nks) break;
+                const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
+                const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128);
+                const int ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
+                bf16x16 bl[NB];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const int row = (wn * WC + 32 * b + r) * 128;
+                    const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
+                    const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
+                    bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
+                                                    12, 13, 14, 15);
                 }
-                __syncthreads();
-                const __amdgpu_buffer_rsrc_t rsP = __builtin_amdgcn_make_buffer_rsrc(
-                    sk.partials, 0, int(uint32_t(gridDim.x) * uint32_t(kSlotBytes)), kRsrcWord3);
-                // at most two: the plan splits no tile over more than three ranges
-                // (a loop with a run-time count here made the compiler spill the
-                // accumulators in the main loop)
-#pragma unroll
-                for (int j = 1; j <= 2; ++j) {
-                    const int r = rho + j;
-                    if (r > last) break;
-                    // one 32 x 32 block at a time (4 loads in flight): the
-                    // accumulators leave few registers free
-#pragma unroll
-                    for (int a = 0; a < 4; ++a)
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-#pragma unroll
-                            for (int g = 0; g < 4; ++g) {
-                                const f32x4 pv = __builtin_bit_cast(
-                                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsP, slot_off(r, a, b, g), 0, kCpolDevice));
-#pragma unroll
-                                for (int i = 0; i < 4; ++i) acc[a][b][4 * g + i] += pv[i];
-                            }
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                }
-            }
-            // ---- y = s * acc + T LA^T: rows scaled by s, then the LoRA up-projection
-            // accumulated on top, with T as stored (no bf16 rounding of T / s)
-#pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x4 sv = *reinterpret_cast<const f32x4*>(s_lds + wm * 128 + 32 * a + 8 * j + 4 * h);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[a][b][4 * j + i] *= sv[i];
-                }
-            if (R > 0) {
-                const char* Ts = smem + cur;
-                const char* Ls = smem + nxt;
-                // T is dense; it is fed to the same SMFMAC as two exactly-2:4
-                // halves with fixed positions (0,1 -> code 0x4; 2,3 -> code 0xE per
-                // group): over channels [16h, 16h+16) of a 32-rank step the even
-                // dwords of the row are positions 0,1 of each group and the odd
-                // dwords positions 2,3.  LA supplies the B operand exactly as W
-                // does in the main loop.
-                const int nks = (R + 31) / 32;  // 1 or 2 (R <= 64)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks >= nks) break;
-                    const int cb0 = 16 * ((4 * ks + h) ^ s128), cb1 = 16 * ((4 * ks + 2 + h) ^ s128);
-                    const int ca0 = 16 * ((4 * ks + 2 * h) ^ s128);
-                    const int ca1 = 16 * ((4 * ks + 2 * h + 1) ^ s128);
-                    bf16x16 bl[NB];
-#pragma unroll
-                    for (int b = 0; b < NB; ++b) {
-                        const int row = (wn * WC + 32 * b + r) * 128;
-                        const bf16x8 lo = lds_read<bf16x8>(Ls, row + cb0);
-                        const bf16x8 hi = lds_read<bf16x8>(Ls, row + cb1);
-                        bl[b] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11,
-                                                        12, 13, 14, 15);
-                    }
-#pragma unroll
-                    for (int a = 0; a < 4; ++a) {
-                        const int row = (wm * 128 + 32 * a + r) * 128;
-                        const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
-                        const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
-                        const bf16x8 te = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.z, t1.x, t1.z});
-                        const bf16x8 to = __builtin_bit_cast(bf16x8, u32x4{t0.y, t0.w, t1.y, t1.w});
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                                te, bl[b], acc[a][b], 0x4444, 0, 0);
-                            acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
-                                to, bl[b], acc[a][b], 0xEEEE, 0, 0);
-                        }
-                    }
-                }
-            }
-
-            // ---- epilogue: interior tiles straight from the accumulators, edge
-            // tiles (columns past N, or N % 8 != 0) through the LDS staging rows
-            if (vec_ok && n0 + TN <= N) {
-                store_block_direct<NB>(acc, rsY, N, m0 + wm * 128, n0 + wn * WC);
-            } else {
-                // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
-                // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
-                // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
-                // Staging rows 4..7 have their 128-byte halves swapped so the two
-                // halves of the wave write different banks.
 #pragma unroll
                 for (int a = 0; a < 4; ++a) {
+                    const int row = (wm * 128 + 32 * a + r) * 128;
+                    const u32x4 t0 = lds_read<u32x4>(Ts, row + ca0);
+                    const u32x4 t1 = lds_read<u32x4>(Ts, row + ca1);
+                    const bf16x8 te = __builtin_bit_cast(bf16x8, u32x4{t0.x, t0.z, t1.x, t1.z});
+                    const bf16x8 to = __builtin_bit_cast(bf16x8, u32x4{t0.y, t0.w, t1.y, t1.w});
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
-#pragma unroll
-                        for (int b = 0; b < NB; ++b)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const int lr = 4 * h + i;  // staging row 0..7
-                                *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
-                                    __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
-                            }
-                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                        __builtin_amdgcn_wave_barrier();
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                        // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
-                        // (of the wave's WC columns)
-                        const int el = fresh_lane();
-                        const int srow = el >> 3;
-                        const int orow = m0 + rbase + srow;
-                        const int ocol = n0 + wn * WC + (el & 7) * 16;
-                        if (orow < M && (el & 7) < 2 * NB) {
-                            const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
-#pragma unroll
-                            for (int i = 0; i < 2; ++i) {
-                                const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
-                                const int col = ocol + 8 * i;
-                                const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
-                                if (vec_ok && col + 8 <= N) {
-                                    __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
-                                } else {
-                                    const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                                    for (int q2 = 0; q2 < 8; ++q2)
-                                        if (col + q2 < N)
-                                            __builtin_amdgcn_raw_buffer_store_b16(
-                                                uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
-                                                yoff + 2u * q2, 0, 0);
-                                }
-                            }
-                        }
-                        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                        __builtin_amdgcn_wave_barrier();
-                        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    for (int b = 0; b < NB; ++b) {
+                        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                            te, bl[b], acc[a][b], 0x4444, 0, 0);
+                        acc[a][b] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(
+                            to, bl[b], acc[a][b], 0xEEEE, 0, 0);
                     }
                 }
             }
         }
+
+        // ---- epilogue: interior tiles straight from the accumulators, edge
+        // tiles (columns past N, or N % 8 != 0) through the LDS staging rows
+        if (vec_ok && n0 + TN <= N) {
+            store_block_direct<NB>(acc, rsY, N, m0 + wm * 128, n0 + wn * WC);
+        } else {
+            // ---- epilogue: y = acc, bf16, 8 rows at a time through LDS ----------
+            // Rows of a 32 x 32 tile held by this lane: 8 (e / 4) + 4 h + e % 4, so
+            // round (a, j) takes e = 4j .. 4j+3 (rows 8j .. 8j+7 of row block a).
+            // Staging rows 4..7 have their 128-byte halves swapped so the two
+            // halves of the wave write different banks.
+    #pragma unroll
+            for (int a = 0; a < 4; ++a) {
+    #pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int rbase = wm * 128 + 32 * a + 8 * j;  // tile row of staging row 0
+    #pragma unroll
+                    for (int b = 0; b < NB; ++b)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int lr = 4 * h + i;  // staging row 0..7
+                            *reinterpret_cast<uint16_t*>(ep + lr * 256 + (((32 * b + r) * 2) ^ (h << 7))) =
+                                __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[a][b][4 * j + i]));
+                        }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                    // lane -> staging row lane / 8, 16 columns from (lane % 8) * 16
+                    // (of the wave's WC columns)
+                    const int el = fresh_lane();
+                    const int srow = el >> 3;
+                    const int orow = m0 + rbase + srow;
+                    const int ocol = n0 + wn * WC + (el & 7) * 16;
+                    if (orow < M && (el & 7) < 2 * NB) {
+                        const int sb = srow * 256 + (((el & 7) * 32) ^ ((srow >> 2) << 7));
+    #pragma unroll
+                        for (int i = 0; i < 2; ++i) {
+                            const u32x4 w4 = lds_read<u32x4>(ep, sb + 16 * i);
+                            const int col = ocol + 8 * i;
+                            const uint32_t yoff = (uint32_t(orow) * uint32_t(N) + uint32_t(col)) * 2u;
+                            if (vec_ok && col + 8 <= N) {
+                                __builtin_amdgcn_raw_buffer_store_b128(w4, rsY, yoff, 0, 0);
+                            } else {
+                                const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+    #pragma unroll
+                                for (int q2 = 0; q2 < 8; ++q2)
+                                    if (col + q2 < N)
+                                        __builtin_amdgcn_raw_buffer_store_b16(
+                                            uint16_t(w[q2 >> 1] >> (16 * (q2 & 1))), rsY,
+                                            yoff + 2u * q2, 0, 0);
+                            }
+                        }
+                    }
+                    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                    __builtin_amdgcn_wave_barrier();
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                }
+            }
+        }
         __syncthreads();  // T / LA slots, s and the staging rows are free
-        // the next unit: its stage 0 is in slot `aft`
+        // the next tile: its stage 0 is in slot `aft`
         const int t_slot = cur;
         cur = aft;
         aft = nxt;
         nxt = t_slot;
         m0 = m0n;
         n0 = n0n;
-        bid = nbid;
-        klen = nlen;
-        role = nrole;
-        ++u;
-        valid = has_next;
     }
 }
 
@@ -718,18 +550,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_sparse32(
 lynx_status launch_gemm_sparse_tiled(const uint16_t* values, const uint8_t* meta,
                                      const float* scale, const uint16_t* T, const uint16_t* W,
                                      const uint16_t* LA, uint16_t* Y, int M, int N, int K, int R,
-                                     const SparsePlan& plan, float* partials, int* flags,
                                      hipStream_t stream) {
-    // persistent: one workgroup per compute unit (the kernel's LDS allows one),
-    // tile width and stream-K split as planned (plan_sparse_gemm)
-    const SkArgs sk{plan.sk_tiles > 0 ? partials : nullptr, plan.sk_tiles > 0 ? flags : nullptr,
-                    plan.dp_tiles, plan.sk_tiles, plan.pairs};
-    if (plan.nb == 3) {
-        hipLaunchKernelGGL(gemm_sparse32<3>, dim3(plan.grid), dim3(NT), 0, stream, values, meta,
-                           scale, T, W, LA, Y, M, N, K, R, sk);
+    // persistent: one workgroup per compute unit (the kernel's LDS allows one).
+    // Tile width 256 or 192: the one whose rounds of tiles over the compute
+    // units cost less (rounds x width; ties to 256), which removes most of the
+    // idle last round when the 256-wide tiles do not divide evenly.
+    int cus = 0;
+    if (device_cu_count(&cus) != LYNX_OK) return LYNX_ERR_DEVICE;
+    const long tm = (M + BM - 1) / BM;
+    auto tiles_for = [&](int tn) { return tm * ((N + tn - 1) / tn); };
+    auto cost = [&](int tn) { return (tiles_for(tn) + cus - 1) / cus * tn; };
+    const bool narrow = cost(192) < cost(256);
+    const long tiles = tiles_for(narrow ? 192 : 256);
+    const int grid = int(tiles < cus ? tiles : cus);
+    if (narrow) {
+        hipLaunchKernelGGL(gemm_sparse32<3>, dim3(grid), dim3(NT), 0, stream, values, meta, scale,
+                           T, W, LA, Y, M, N, K, R);
     } else {
-        hipLaunchKernelGGL(gemm_sparse32<4>, dim3(plan.grid), dim3(NT), 0, stream, values, meta,
-                           scale, T, W, LA, Y, M, N, K, R, sk);
+        hipLaunchKernelGGL(gemm_sparse32<4>, dim3(grid), dim3(NT), 0, stream, values, meta, scale,
+                           T, W, LA, Y, M, N, K, R);
     }
     return launch_status();
 }

@@ -105,7 +105,7 @@ template <int RT, int ROWT, int NW, bool HALF>
 __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ LB, int M, int K,
     uint16_t* __restrict__ values, uint8_t* __restrict__ meta, float* __restrict__ scale,
-    uint16_t* __restrict__ T, int* __restrict__ zero_flags, int nzero) {
+    uint16_t* __restrict__ T) {
     constexpr int R = RT * 16;
     constexpr int kWgRows = kRows * ROWT;
     __shared__ double red_norm[NW][kWgRows][2];
@@ -122,9 +122,6 @@ __global__ __launch_bounds__(NW * 64) void sparsify_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
-    // the sparse GEMM's stream-K flags start every layer at zero
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < nzero; i += blockDim.x) zero_flags[i] = 0;
     const int r = lane & 15;
     const int q = lane >> 4;
     const int m0 = blockIdx.x * kWgRows;
@@ -343,30 +340,28 @@ constexpr float kRowtCost[4] = {0.f, 1.0f, 1.45f, 1.8f};
 
 template <int RT, bool HALF>
 void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uint16_t* LB,
-               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, int* zf, int nz,
-               hipStream_t stream) {
+               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, hipStream_t stream) {
     const int nw = rowt == 1 ? 8 : 4;
     const dim3 grid((M + kRows * rowt - 1) / (kRows * rowt)), block(64 * (nchunks < nw ? nchunks : nw));
     if (rowt == 1) {
         hipLaunchKernelGGL((sparsify_kernel<RT, 1, 8, HALF>), grid, block, 0, stream, X, LB, M, K,
-                           values, meta, scale, T, zf, nz);
+                           values, meta, scale, T);
     } else if (rowt == 2) {
         hipLaunchKernelGGL((sparsify_kernel<RT, 2, 4, HALF>), grid, block, 0, stream, X, LB, M, K,
-                           values, meta, scale, T, zf, nz);
+                           values, meta, scale, T);
     } else {
         hipLaunchKernelGGL((sparsify_kernel<RT, 3, 4, HALF>), grid, block, 0, stream, X, LB, M, K,
-                           values, meta, scale, T, zf, nz);
+                           values, meta, scale, T);
     }
 }
 
 template <int RT>
 void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uint16_t* LB,
-               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, int* zf, int nz,
-               hipStream_t stream) {
+               uint16_t* values, uint8_t* meta, float* scale, uint16_t* T, hipStream_t stream) {
     if (K % kChunk == 0) {
-        launch_rt<RT, false>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zf, nz, stream);
+        launch_rt<RT, false>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
     } else {
-        launch_rt<RT, true>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zf, nz, stream);
+        launch_rt<RT, true>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
     }
 }
 
@@ -374,7 +369,7 @@ void launch_rt(int rowt, int M, int K, int nchunks, const uint16_t* X, const uin
 
 lynx_status launch_sparsify(const uint16_t* X, const uint16_t* LB, int M, int K, int R,
                             uint16_t* values, uint8_t* meta, float* scale, uint16_t* T,
-                            int* zero_flags, int nzero, hipStream_t stream) {
+                            hipStream_t stream) {
     const int nchunks = (K + kChunk - 1) / kChunk;
     // Row tiles per workgroup: the fewest rounds of workgroups over the compute
     // units, weighted by the measured cost of a workgroup (one tile when there
@@ -396,19 +391,19 @@ lynx_status launch_sparsify(const uint16_t* X, const uint16_t* LB, int M, int K,
     }
     switch (R / 16) {
         case 0:
-            launch_rt<0>(1, M, K, nchunks, X, LB, values, meta, scale, T, zero_flags, nzero, stream);
+            launch_rt<0>(1, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 1:
-            launch_rt<1>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zero_flags, nzero, stream);
+            launch_rt<1>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 2:
-            launch_rt<2>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zero_flags, nzero, stream);
+            launch_rt<2>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         case 3:
-            launch_rt<3>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zero_flags, nzero, stream);
+            launch_rt<3>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
         default:
-            launch_rt<4>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, zero_flags, nzero, stream);
+            launch_rt<4>(rowt, M, K, nchunks, X, LB, values, meta, scale, T, stream);
             break;
     }
     return launch_status();

@@ -5,7 +5,6 @@
 #include <cstring>
 
 #include "lynx_internal.h"
-#include "lynx_probe.h"
 
 namespace lynx {
 
@@ -37,23 +36,17 @@ bool dims_ok(int64_t M, int64_t N, int64_t K) {
 }
 
 struct WorkspaceLayout {
-    size_t values, meta, scale, T, partials, flags, total;
-    SparsePlan plan;  // the GEMM's schedule, stream-K allowed
+    size_t values, meta, scale, T, total;
 };
 
-// Packed operand, s, T, then the GEMM's stream-K partial sums and flags
-// (empty when its plan has no stream-K tiles).
-WorkspaceLayout layout_for(int64_t M, int64_t N, int64_t K, int64_t R) {
+WorkspaceLayout layout_for(int64_t M, int64_t K, int64_t R) {
     const size_t Mp = size_t((M + 15) / 16) * 16;  // packed operand rows, whole 16-row tiles
-    WorkspaceLayout L{};
-    L.plan = plan_sparse_gemm(int(M), int(N), int(K), true);
+    WorkspaceLayout L;
     L.values = 0;
     L.meta = L.values + round_up256(Mp * size_t(K / 2) * 2);
     L.scale = L.meta + round_up256(Mp * size_t(K / 8));
     L.T = L.scale + round_up256(size_t(M) * 4);
-    L.partials = L.T + round_up256(size_t(M) * size_t(R) * 2);
-    L.flags = L.partials + L.plan.partial_bytes;
-    L.total = L.flags + L.plan.flag_bytes;
+    L.total = L.T + round_up256(size_t(M) * size_t(R) * 2);
     return L;
 }
 }  // namespace
@@ -116,28 +109,25 @@ lynx_status validate_sparse_layer(const uint16_t* X, const uint16_t* W, const ui
     return LYNX_OK;
 }
 
-size_t sparse_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R) {
-    return layout_for(M, N, K, R).total;
+size_t sparse_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+    return layout_for(M, K, R).total;
 }
 
 // the sparse layer on validated arguments
 lynx_status run_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
                              const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K,
                              int64_t R, void* workspace, hipStream_t s) {
-    const WorkspaceLayout L = layout_for(M, N, K, R);
+    const WorkspaceLayout L = layout_for(M, K, R);
     char* ws = static_cast<char*>(workspace);
     uint16_t* values = reinterpret_cast<uint16_t*>(ws + L.values);
     uint8_t* meta = reinterpret_cast<uint8_t*>(ws + L.meta);
     float* scale = reinterpret_cast<float*>(ws + L.scale);
     uint16_t* T = R > 0 ? reinterpret_cast<uint16_t*>(ws + L.T) : nullptr;
-    float* partials = reinterpret_cast<float*>(ws + L.partials);
-    int* flags = reinterpret_cast<int*>(ws + L.flags);
-    // the sparsifier also clears the GEMM's stream-K flags
     lynx_status st = launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values,
-                                     meta, scale, T, flags, L.plan.sk_tiles, s);
+                                     meta, scale, T, s);
     if (st != LYNX_OK) return st;
     return launch_gemm_sparse(values, meta, scale, T, W, R > 0 ? LA : nullptr, Y, int(M), int(N),
-                              int(K), int(R), L.plan, partials, flags, s);
+                              int(K), int(R), s);
 }
 }  // namespace lynx
 
@@ -157,7 +147,7 @@ const char* lynx_status_string(lynx_status s) {
             return "LYNX_ERR_UNSUPPORTED_DEVICE: the current device is not gfx950";
         case LYNX_ERR_SCRATCH:
             return "LYNX_ERR_SCRATCH: the problem needs more workspace than the library's "
-                   "static scratch array holds (128 MiB); call lynx_linear_sparse_lora with a "
+                   "static scratch array holds (64 MiB); call lynx_linear_sparse_lora with a "
                    "workspace instead";
     }
     return "LYNX_ERR_UNKNOWN";
@@ -165,10 +155,9 @@ const char* lynx_status_string(lynx_status s) {
 
 int lynx_version(void) { return 100; }
 
-size_t lynx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R) {
-    if (!dims_ok(M, N, K) || !rank_ok(R)) return 0;
-    if (M == 0 || N == 0) return 256;  // a no-op call; any valid workspace
-    return sparse_workspace_bytes(M, N, K, R);
+size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R) {
+    if (!dims_ok(M, 1, K) || !rank_ok(R)) return 0;
+    return layout_for(M, K, R).total;
 }
 
 lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB, int64_t M, int64_t K, int64_t R,
@@ -184,49 +173,7 @@ lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB, int64_t M, int6
     lynx_status st = check_device();
     if (st != LYNX_OK) return st;
     return launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values, meta, scale,
-                           R > 0 ? T : nullptr, nullptr, 0, static_cast<hipStream_t>(stream));
-}
-
-lynx_status lynx_probe_sparse_plan(int64_t M, int64_t N, int64_t K, int32_t with_sk, int32_t cus,
-                                   int64_t* out) {
-    if (!dims_ok(M, N, K) || M < 1 || N < 1 || cus < 1) return LYNX_ERR_SHAPE;
-    if (!out) return LYNX_ERR_NULL;
-    const SparsePlan p = plan_sparse_gemm_for(int(M), int(N), int(K), with_sk != 0, cus);
-    const int64_t v[8] = {p.tiled ? 1 : 0, p.tiled ? 64 * p.nb : 64, p.grid, p.dp_tiles,
-                          p.sk_tiles, p.pairs, int64_t(p.partial_bytes), int64_t(p.flag_bytes)};
-    for (int i = 0; i < 8; ++i) out[i] = v[i];
-    return LYNX_OK;
-}
-
-lynx_status lynx_probe_gemm_sparse_ws(const uint16_t* values, const uint8_t* meta,
-                                      const float* scale, const uint16_t* T, const uint16_t* W,
-                                      const uint16_t* LA, uint16_t* Y, int64_t M, int64_t N,
-                                      int64_t K, int64_t R, void* workspace,
-                                      size_t workspace_bytes, lynx_stream_t stream) {
-    if (!dims_ok(M, N, K) || !rank_ok(R)) return LYNX_ERR_SHAPE;
-    if (M == 0 || N == 0) return LYNX_OK;
-    if (!values || !meta || !scale || !W || !Y) return LYNX_ERR_NULL;
-    if (R > 0 && (!T || !LA)) return LYNX_ERR_NULL;
-    if (!aligned16(values) || !aligned16(meta) || !aligned16(scale) || !aligned16(W) ||
-        !aligned16(Y))
-        return LYNX_ERR_ALIGN;
-    if (R > 0 && (!aligned16(T) || !aligned16(LA))) return LYNX_ERR_ALIGN;
-    lynx_status st = check_device();
-    if (st != LYNX_OK) return st;
-    const SparsePlan plan = plan_sparse_gemm(int(M), int(N), int(K), true);
-    if (plan.sk_tiles > 0 && (!workspace || workspace_bytes < plan.partial_bytes + plan.flag_bytes))
-        return LYNX_ERR_WORKSPACE;
-    if (plan.sk_tiles > 0 && (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return LYNX_ERR_ALIGN;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    float* partials = static_cast<float*>(workspace);
-    int* flags = reinterpret_cast<int*>(static_cast<char*>(workspace) + plan.partial_bytes);
-    if (plan.sk_tiles > 0) {
-        st = launch_zero_ints(flags, plan.sk_tiles, s);
-        if (st != LYNX_OK) return st;
-    }
-    return launch_gemm_sparse(values, meta, scale, R > 0 ? T : nullptr, W, R > 0 ? LA : nullptr,
-                              Y, int(M), int(N), int(K), int(R), plan, partials, flags, s);
+                           R > 0 ? T : nullptr, static_cast<hipStream_t>(stream));
 }
 
 lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t* meta,
@@ -244,10 +191,8 @@ lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t
     if (R > 0 && (!aligned16(T) || !aligned16(LA))) return LYNX_ERR_ALIGN;
     lynx_status st = check_device();
     if (st != LYNX_OK) return st;
-    // no workspace here: whole tiles only
-    const SparsePlan plan = plan_sparse_gemm(int(M), int(N), int(K), false);
     return launch_gemm_sparse(values, meta, scale, R > 0 ? T : nullptr, W, R > 0 ? LA : nullptr,
-                              Y, int(M), int(N), int(K), int(R), plan, nullptr, nullptr,
+                              Y, int(M), int(N), int(K), int(R),
                               static_cast<hipStream_t>(stream));
 }
 
@@ -261,7 +206,7 @@ lynx_status validate_sparse(const uint16_t* X, const uint16_t* W, const uint16_t
                             bool* noop) {
     lynx_status st = validate_sparse_layer(X, W, LA, LB, Y, M, N, K, R, noop);
     if (st != LYNX_OK || *noop) return st;
-    if (!workspace || workspace_bytes < layout_for(M, N, K, R).total) return LYNX_ERR_WORKSPACE;
+    if (!workspace || workspace_bytes < layout_for(M, K, R).total) return LYNX_ERR_WORKSPACE;
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return LYNX_ERR_ALIGN;
     return LYNX_OK;
 }
@@ -314,7 +259,7 @@ size_t lynx_sequence_workspace_bytes(const lynx_layer* layers, int64_t n) {
         } else if (L.mode == LYNX_LAYER_SPARSE_LORA) {
             if (!dims_ok(L.M, L.N, L.K) || !rank_ok(L.R)) return 0;
             if (L.M > 0 && L.N > 0) {
-                const size_t b = sparse_workspace_bytes(L.M, L.N, L.K, L.R);
+                const size_t b = layout_for(L.M, L.K, L.R).total;
                 if (b > need) need = b;
             }
         } else {

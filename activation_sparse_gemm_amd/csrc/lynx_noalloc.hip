@@ -59,9 +59,8 @@ extern "C" lynx_status lynx_linear_sparse_lora_noalloc(const uint16_t* X, const 
     lynx_status st = validate_sparse_layer(X, W, LA, LB, Y, M, N, K, R, &noop);
     if (st != LYNX_OK || noop) return st;
     // K1 writes every byte of the packed operand (padding rows included), s
-    // and T that K2 reads, and clears K2's stream-K flags, so nothing in the
-    // array needs clearing here
-    if (sparse_workspace_bytes(M, N, K, R) > LYNX_SCRATCH_BYTES) return LYNX_ERR_SCRATCH;
+    // and T that K2 reads, so nothing in the array needs clearing
+    if (sparse_workspace_bytes(M, K, R) > LYNX_SCRATCH_BYTES) return LYNX_ERR_SCRATCH;
     st = check_device();
     if (st != LYNX_OK) return st;
     char* ws = nullptr;

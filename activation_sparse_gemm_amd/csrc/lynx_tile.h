@@ -13,40 +13,6 @@ constexpr int BM = 256, NT = 256, GROUP_M = 8;
 __device__ __forceinline__ int swz64(int row) { return ((row >> 1) & 3) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz128(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-// Tile order.  Workgroup ids go to the 8 XCDs round-robin, so the whole-tile
-// schedule (tile index bid = blockIdx.x + i * gridDim.x) gives XCD bid % 8 the
-// contiguous stretch ("region") xcd * per + min(xcd, rem) + ... of the order
-// position v, and v is rasterized in groups of GROUP_M tile-rows: the ~32
-// workgroups of one XCD then work on nearby tiles and share A rows and W rows
-// in that XCD's L2.
-__device__ __forceinline__ void tile_at(int v, int tiles_m, int tiles_n, int& tm, int& tn) {
-    const int group_size = GROUP_M * tiles_n;
-    const int group = v / group_size;
-    const int first_m = group * GROUP_M;
-    const int gm = min(tiles_m - first_m, GROUP_M);
-    const int in = v - group * group_size;
-    tm = first_m + in % gm;
-    tn = in / gm;
-}
-
-// Stream-K tile t (the tiles after the whole ones, split along K): the
-// stream-K ranges run XCD-major, so the tiles XCD 0's ranges share come first,
-// then XCD 1's, ...; each XCD's share fills the rest of its region (the
-// positions its whole tiles leave free), keeping its tiles nearby as well.
-// A bijection onto the positions the whole tiles do not take, for any sizes.
-__device__ __forceinline__ int sk_tile_position(int t, int ntiles, int dp_tiles) {
-    const int per = ntiles >> 3, rem = ntiles & 7;
-    int x = 0;
-    for (; x < 7; ++x) {
-        const int n = per + (x < rem ? 1 : 0);                       // region size
-        const int d = dp_tiles > x ? (dp_tiles - x + 7) >> 3 : 0;    // its whole tiles
-        if (t < n - d) break;
-        t -= n - d;
-    }
-    const int d = dp_tiles > x ? (dp_tiles - x + 7) >> 3 : 0;
-    return x * per + min(x, rem) + d + t;
-}
-
 __device__ __forceinline__ void tile_of(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
     const int ntiles = tiles_m * tiles_n;
     const int xcd = bid & 7, slot = bid >> 3;

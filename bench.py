@@ -520,7 +520,7 @@ def fusion_prototype(rounds: int, calls: int, nsets: int) -> dict:
                                                seed=100 + 10 * s, R=base.R, name=base.name)
             d = dict(X=to_dev(L.X), W=to_dev(L.W), LA=to_dev(L.LA), LB=to_dev(L.LB))
             d["Y"] = torch.empty((L.M, L.N), dtype=torch.bfloat16, device=dev)
-            d["ws"] = torch.empty(lynx.workspace_bytes(L.M, L.N, L.K, L.R), dtype=torch.uint8,
+            d["ws"] = torch.empty(lynx.workspace_bytes(L.M, L.K, L.R), dtype=torch.uint8,
                                   device=dev)
             d["packed"] = lynx.sparsify(d["X"], d["LB"])
             sets.append(d)
@@ -623,7 +623,7 @@ def main():
                                                seed=100 + 10 * s + j, R=base.R, name=base.name)
             X, W, LA, LB = to_dev(L.X), to_dev(L.W), to_dev(L.LA), to_dev(L.LB)
             M, K, N, R = L.M, L.K, L.N, L.R
-            ws = torch.empty(lynx.workspace_bytes(M, N, K, R), dtype=torch.uint8, device=dev)
+            ws = torch.empty(lynx.workspace_bytes(M, K, R), dtype=torch.uint8, device=dev)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             Yd = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             packed = lynx.sparsify(X, LB)

@@ -90,17 +90,11 @@ const char* lynx_status_string(lynx_status s);
 int lynx_version(void);
 
 /*
- * Bytes of device workspace lynx_linear_sparse_lora needs for an (M, N, K, R)
- * problem: the packed operand (values Mp*K bytes, meta Mp*K/8, scale 4M), T
- * (2MR) and, when the sparse GEMM splits tiles along K over the compute units
- * (stream-K), one slot of fp32 partial sums per compute unit (64 KiB per 64
- * tile columns: 256 KiB with 256-wide tiles) and one int per split tile, each
- * part 256-byte aligned.  Whether the GEMM splits depends on the shape and on
- * the current device's compute-unit count (256 is assumed where no device can
- * be queried), so ask on the device the layer will run on.  Returns 0 for
- * invalid sizes; 256 when M or N is 0.
+ * Bytes of device workspace lynx_linear_sparse_lora needs for an (M, K, R)
+ * problem: the packed operand (values Mp*K bytes, meta Mp*K/8, scale 4M) and
+ * T (2MR), each 256-byte aligned.  Returns 0 for invalid sizes.
  */
-size_t lynx_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t R);
+size_t lynx_workspace_bytes(int64_t M, int64_t K, int64_t R);
 
 /*
  * lynx_sparsify - online activation sparsification and LoRA down-projection.
@@ -124,13 +118,8 @@ lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB,
  * epilogue adds T LA^T and applies s, with fp32 accumulation and a bf16
  * (round-to-nearest-even) store.
  * Inputs: X [M][K], W [N][K], LA [N][R], LB [R][K] (LA, LB NULL iff R == 0).
- * Output: Y [M][N] bf16.  workspace: >= lynx_workspace_bytes(M, N, K, R)
- * bytes, 256-byte aligned, contents on entry irrelevant, clobbered.
- * Results are deterministic: the same inputs on the same device give the same
- * bits, whatever the workspace held (stream-K partial sums are added in a
- * fixed order).  They can differ in the last bits from
- * lynx_linear_sparse_lora_packed, which has no workspace and never splits
- * tiles along K.
+ * Output: Y [M][N] bf16.  workspace: >= lynx_workspace_bytes(M, K, R) bytes,
+ * 256-byte aligned, contents on entry irrelevant, clobbered.
  */
 lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W,
                                     const uint16_t* LA, const uint16_t* LB, uint16_t* Y,
@@ -143,14 +132,13 @@ lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W,
  * workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same inputs, output, kernels and results as
- * lynx_linear_sparse_lora; the packed operand, s, T and the GEMM's stream-K
- * partial sums go to a static device
- * array of the library (128 MiB per device, LYNX_SCRATCH_BYTES), allocated
+ * lynx_linear_sparse_lora; the packed operand, s and T go to a static device
+ * array of the library (64 MiB per device, LYNX_SCRATCH_BYTES), allocated
  * when the library's code is loaded on a device and held until the process
  * ends.  The call itself allocates nothing, on the device or the host.
- *   - Problems whose lynx_workspace_bytes(M, N, K, R) exceeds
- *     LYNX_SCRATCH_BYTES return LYNX_ERR_SCRATCH (the workloads of the DiT
- *     block at M = 9216 fit up to K = 3072; M = 4096 fits K = 12288).
+ *   - Problems whose lynx_workspace_bytes(M, K, R) exceeds LYNX_SCRATCH_BYTES
+ *     return LYNX_ERR_SCRATCH (e.g. M = 4096 fits up to K = 12288 with
+ *     R = 64; M = 9216 fits up to K = 6144).
  *   - Every call on a device shares that device's array, which keeps the last
  *     call's contents (each call writes every byte it reads before reading
  *     it).  Calls that overlap on one device - on different streams, or from
@@ -160,7 +148,7 @@ lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W,
  *     (hipGetSymbolAddress) and keeps it; a failure there returns
  *     LYNX_ERR_DEVICE.
  */
-#define LYNX_SCRATCH_BYTES ((size_t)128 << 20)
+#define LYNX_SCRATCH_BYTES ((size_t)64 << 20)
 
 lynx_status lynx_linear_sparse_lora_noalloc(const uint16_t* X, const uint16_t* W,
                                             const uint16_t* LA, const uint16_t* LB, uint16_t* Y,
@@ -212,7 +200,7 @@ typedef struct lynx_layer {
 
 /*
  * Bytes of workspace lynx_linear_sequence needs: the largest
- * lynx_workspace_bytes(M, N, K, R) over its sparse layers (0 if there are none,
+ * lynx_workspace_bytes(M, K, R) over its sparse layers (0 if there are none,
  * or if any layer is invalid).  layers: host array of n descriptors.
  */
 size_t lynx_sequence_workspace_bytes(const lynx_layer* layers, int64_t n);

@@ -49,38 +49,6 @@ lynx_status lynx_probe_mfma(int which, int abid, const uint16_t* a, const uint16
 lynx_status lynx_probe_mfma_rate(int which, int iters, int grid, float* sink, uint64_t* stamps,
                                  lynx_stream_t stream);
 
-/*
- * The sparse GEMM's schedule for an (M, N, K) layer on a device of `cus`
- * compute units (host only, nothing is launched), with stream-K allowed as
- * lynx_linear_sparse_lora plans it (with_sk = 1) or not, as
- * lynx_linear_sparse_lora_packed plans it (with_sk = 0).  out: 8 int64,
- *   [0] 1 for the tiled kernel, 0 for the 64 x 64 kernel; [1] tile width
- *   (256 or 192); [2] workgroups; [3] whole tiles; [4] stream-K tiles;
- *   [5] their 64-channel stage pairs; [6] workspace bytes of the partial
- *   sums; [7] workspace bytes of the flags.
- * Stream-K range rho (0 <= rho < workgroups) takes the stage pairs
- * floor(rho * pairs / grid) .. floor((rho + 1) * pairs / grid) - 1 of the
- * stream-K tiles, tile by tile.  LYNX_ERR_SHAPE for sizes the layer rejects
- * or cus < 1; LYNX_ERR_NULL for out == NULL.
- */
-lynx_status lynx_probe_sparse_plan(int64_t M, int64_t N, int64_t K, int32_t with_sk, int32_t cus,
-                                   int64_t* out);
-
-/*
- * The sparse GEMM alone, with the schedule lynx_linear_sparse_lora uses
- * (stream-K included), on an operand packed as for
- * lynx_linear_sparse_lora_packed (same arguments and checks).  `workspace`
- * holds the stream-K partial sums and flags: at least out[6] + out[7] bytes
- * of lynx_probe_sparse_plan (lynx_workspace_bytes(M, N, K, R) always
- * suffices), 256-byte aligned; its flags are cleared by a small kernel first.
- * Used to time the layer's GEMM apart from the sparsifier.
- */
-lynx_status lynx_probe_gemm_sparse_ws(const uint16_t* values, const uint8_t* meta,
-                                      const float* scale, const uint16_t* T, const uint16_t* W,
-                                      const uint16_t* LA, uint16_t* Y, int64_t M, int64_t N,
-                                      int64_t K, int64_t R, void* workspace,
-                                      size_t workspace_bytes, lynx_stream_t stream);
-
 #ifdef __cplusplus
 }
 #endif

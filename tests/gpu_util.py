@@ -101,7 +101,7 @@ def sparse_lora(X, W, LA=None, LB=None):
     (M, K), N = X.shape, W.shape[0]
     R = 0 if LA is None else LA.shape[1]
     return lynx.linear_sparse_lora(X, W, LA, LB, Y=nan_bf16((M, N)),
-                                   workspace=poisoned_bytes(lynx.workspace_bytes(M, N, K, R)))
+                                   workspace=poisoned_bytes(lynx.workspace_bytes(M, K, R)))
 
 
 def sparse_lora_noalloc(X, W, LA=None, LB=None):

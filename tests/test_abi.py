@@ -50,21 +50,17 @@ def test_status_strings():
 
 
 def test_workspace_bytes():
-    # MLP-up (three full rounds of tiles: no stream-K region)
-    ws = _abi.workspace_bytes(4096, 12288, 3072, 64)
+    ws = _abi.workspace_bytes(4096, 3072, 64)
     # values M*K + meta M*K/8 + scale 4M + T 2MR, each 256-aligned
     assert ws == 4096 * 3072 + 4096 * 3072 // 8 + 4096 * 4 + 4096 * 64 * 2
     # M = 3 -> 16 stored rows: values 16*128 B, meta 16*16 B, scale and T rounded to 256 B
-    assert _abi.workspace_bytes(3, 16, 128, 16) == 2048 + 256 + 256 + 256
-    assert _abi.workspace_bytes(16, 16, 100, 0) == 0      # K not a multiple of 64
-    assert _abi.workspace_bytes(16, 16, 96, 0) == 0
-    assert _abi.workspace_bytes(16, 16, 64, 0) > 0       # K % 64 == 0 is enough
-    assert _abi.workspace_bytes(16, 16, 192, 16) > 0
-    assert _abi.workspace_bytes(16, 16, 128, 8) == 0      # unsupported rank
-    assert _abi.workspace_bytes(-1, 16, 128, 0) == 0
-    assert _abi.workspace_bytes(16, -1, 128, 0) == 0
-    assert _abi.workspace_bytes(0, 16, 128, 16) == 256    # no-op shapes
-    assert _abi.workspace_bytes(16, 0, 128, 16) == 256
+    assert _abi.workspace_bytes(3, 128, 16) == 2048 + 256 + 256 + 256
+    assert _abi.workspace_bytes(16, 100, 0) == 0      # K not a multiple of 64
+    assert _abi.workspace_bytes(16, 96, 0) == 0
+    assert _abi.workspace_bytes(16, 64, 0) > 0       # K % 64 == 0 is enough
+    assert _abi.workspace_bytes(16, 192, 16) > 0
+    assert _abi.workspace_bytes(16, 128, 8) == 0      # unsupported rank
+    assert _abi.workspace_bytes(-1, 128, 0) == 0
 
 
 def call_sparsify(X=A, LB=A, M=16, K=128, R=16, values=A, meta=A, scale=A, T=A):
@@ -99,7 +95,7 @@ def test_linear_validation(kw, status):
 
 
 def test_linear_workspace_exact_boundary():
-    need = _abi.workspace_bytes(16, 16, 128, 16)
+    need = _abi.workspace_bytes(16, 128, 16)
     assert call_linear(wsb=need - 1) == WORKSPACE
 
 
@@ -111,8 +107,8 @@ def call_noalloc(X=A, W=A, LA=A, LB=A, Y=A, M=16, N=16, K=128, R=16):
     (dict(K=160), SHAPE), (dict(R=17), SHAPE), (dict(M=1 << 25), SHAPE),
     (dict(W=None), NULL), (dict(LB=None), NULL), (dict(Y=A + 2), ALIGN),
     (dict(M=0), OK), (dict(N=0), OK),
-    # the static scratch array holds LYNX_SCRATCH_BYTES = 128 MiB
-    (dict(M=9216, N=3072, K=12288, R=64), SCRATCH), (dict(M=16384, K=8192, R=0), SCRATCH),
+    # the static scratch array holds LYNX_SCRATCH_BYTES = 64 MiB
+    (dict(M=9216, K=12288, R=64), SCRATCH), (dict(M=8192, K=8192, R=0), SCRATCH),
 ])
 def test_noalloc_validation(kw, status):
     assert call_noalloc(**kw) == status
@@ -121,21 +117,17 @@ def test_noalloc_validation(kw, status):
 def test_noalloc_scratch_limit_is_the_workspace_size():
     """A problem is accepted exactly when its workspace fits the array."""
     import torch
-    # (M, N, K, R); N = 16 plans whole tiles only, N = 3072 splits M = 4096 x
-    # K = 12288 along K (stream-K: 64 MiB of partial sums on top)
-    fits = [(4096, 16, 12288, 64), (4096, 16, 3072, 64), (9216, 3072, 3072, 64),
-            (14496, 16, 8192, 16), (4096, 12288, 3072, 64), (4096, 3072, 12288, 64),
-            (9216, 16, 12288, 64)]
-    too_big = [(14497, 16, 8192, 16), (9216, 3072, 12288, 64)]
-    for M, N, K, R in fits:
-        assert 0 < _abi.workspace_bytes(M, N, K, R) <= _abi.SCRATCH_BYTES
-    for M, N, K, R in too_big:
-        assert _abi.workspace_bytes(M, N, K, R) > _abi.SCRATCH_BYTES
-        assert call_noalloc(M=M, N=N, K=K, R=R) == SCRATCH
+    fits = [(4096, 12288, 64), (4096, 3072, 64), (7248, 8192, 16), (9520, 6144, 64)]
+    too_big = [(9216, 12288, 64), (7249, 8192, 16), (9521, 6144, 64)]
+    for M, K, R in fits:
+        assert 0 < _abi.workspace_bytes(M, K, R) <= _abi.SCRATCH_BYTES
+    for M, K, R in too_big:
+        assert _abi.workspace_bytes(M, K, R) > _abi.SCRATCH_BYTES
+        assert call_noalloc(M=M, K=K, R=R) == SCRATCH
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
-    for M, N, K, R in fits:
-        assert call_noalloc(M=M, N=N, K=K, R=R) == UNSUPPORTED
+    for M, K, R in fits:
+        assert call_noalloc(M=M, K=K, R=R) == UNSUPPORTED
 
 
 def call_packed(v=A, m=A, s=A, T=A, W=A, LA=A, Y=A, M=16, N=16, K=128, R=16):
@@ -193,7 +185,7 @@ def test_shape_limit_of_32bit_offsets_rejects(M, N, K):
     assert call_sequence(layers_of((M, N, K, 16, SP))) == SHAPE
     if (M + 256) * K >= LIMIT:
         assert call_sparsify(M=M, K=K) == SHAPE
-        assert _abi.workspace_bytes(M, N, K, 16) == 0
+        assert _abi.workspace_bytes(M, K, 16) == 0
 
 
 @pytest.mark.parametrize("M,N,K", [
@@ -204,7 +196,7 @@ def test_shape_limit_of_32bit_offsets_admits(M, N, K):
     """One row or column below the limit passes validation: without a GPU the
     call stops at the device check (it never launches)."""
     import torch
-    assert _abi.workspace_bytes(M, N, K, 16) > 0
+    assert _abi.workspace_bytes(M, K, 16) > 0
     if torch.cuda.is_available():
         pytest.skip("a GPU is present: valid fake pointers must not reach a launch")
     assert call_linear(M=M, N=N, K=K, wsb=1 << 40) == UNSUPPORTED
@@ -255,8 +247,7 @@ SP, DN = _abi.LAYER_SPARSE_LORA, _abi.LAYER_DENSE
 def test_sequence_workspace_bytes_is_the_largest_sparse_layer():
     arr = layers_of((9216, 9216, 3072, 64, SP), (9216, 3072, 3072, 64, DN),
                     (9216, 12288, 3072, 64, SP), (9216, 3072, 12288, 64, SP))
-    want = max(_abi.workspace_bytes(9216, 9216, 3072, 64), _abi.workspace_bytes(9216, 12288, 3072, 64),
-               _abi.workspace_bytes(9216, 3072, 12288, 64))
+    want = max(_abi.workspace_bytes(9216, 3072, 64), _abi.workspace_bytes(9216, 12288, 64))
     assert _abi.lib().lynx_sequence_workspace_bytes(arr, 4) == want
     assert _abi.lib().lynx_sequence_workspace_bytes(layers_of((16, 16, 128, 0, DN)), 1) == 0
     assert _abi.lib().lynx_sequence_workspace_bytes(layers_of((16, 16, 100, 0, DN)), 1) == 0
@@ -276,7 +267,7 @@ def test_sequence_validation():
     assert call_sequence(layers_of(good, (16, 16, 96, 16, SP))) == SHAPE
     assert call_sequence(layers_of(good, (16, 16, 128, 0, 5))) == SHAPE
     assert call_sequence(layers_of((16, 16, 128, 16, SP)), ws=None) == WORKSPACE
-    assert call_sequence(layers_of(good), wsb=_abi.workspace_bytes(16, 16, 128, 16) - 1) == WORKSPACE
+    assert call_sequence(layers_of(good), wsb=_abi.workspace_bytes(16, 128, 16) - 1) == WORKSPACE
     assert call_sequence(layers_of(good), ws=B + 16) == ALIGN
     arr = layers_of(good, (16, 16, 128, 0, DN))
     arr[1].X = A + 2

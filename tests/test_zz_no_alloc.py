@@ -39,25 +39,18 @@ def check_against_workspace_entry(M, K, N, R, seed):
 
 
 def test_noalloc_two_calls_second_smaller():
-    # the QKV layer, whose GEMM splits tiles along K (stream-K: 78 MB of
-    # scratch with the partial sums), the MLP-up layer (14.7 MB, whole tiles),
-    # then a smaller ragged one that runs the 192-wide tiles, then one small
-    # enough for the 64 x 64 kernels
-    assert lynx._abi.sparse_plan(4096, 9216, 3072, True,
-                                 torch.cuda.get_device_properties(0).multi_processor_count)["sk_tiles"] > 0
-    check_against_workspace_entry(4096, 3072, 9216, 64, seed=4)
+    # the MLP-up layer (14.7 MB of scratch), then a smaller ragged one that
+    # runs the 192-wide tiles, then one small enough for the 64 x 64 kernels
     check_against_workspace_entry(4096, 3072, 12288, 64, seed=1)
     check_against_workspace_entry(1000, 640, 1100, 48, seed=2)
     check_against_workspace_entry(100, 256, 130, 0, seed=3)
 
 
 def test_noalloc_rejects_problems_beyond_the_array():
-    # the block's MLP-down layer: packed operand (127 MB) and stream-K partial
-    # sums (64 MiB) exceed the 128 MiB array
     X = torch.zeros((9216, 12288), dtype=torch.bfloat16, device="cuda")
-    W = torch.zeros((3072, 12288), dtype=torch.bfloat16, device="cuda")
-    LA = torch.zeros((3072, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((16, 12288), dtype=torch.bfloat16, device="cuda")
+    LA = torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda")
     LB = torch.zeros((64, 12288), dtype=torch.bfloat16, device="cuda")
-    assert lynx.workspace_bytes(9216, 3072, 12288, 64) > lynx.SCRATCH_BYTES
+    assert lynx.workspace_bytes(9216, 12288, 64) > lynx.SCRATCH_BYTES
     with pytest.raises(lynx.LynxError, match="LYNX_ERR_SCRATCH"):
         lynx.linear_sparse_lora_noalloc(X, W, LA, LB)
