@@ -733,6 +733,8 @@ def main():
         "pct_dense_peak": round(100 * tflops / PEAK_DENSE_BF16_TFLOPS, 2),
         "speedup_vs_dense": round(ms_dense / ms_sparse_i, 3),
         "speedup_vs_torch_matmul": round(ms_torch / ms_sparse_i, 3),
+        # against the faster of the two dense layers (the library's and hipBLASLt)
+        "speedup_vs_best_dense": round(min(ms_dense, ms_torch) / ms_sparse_i, 3),
         "interleaved_ms": {"sparse_layer": round(ms_sparse_i, 5), "dense_layer": round(ms_dense, 5),
                            "torch_matmul": round(ms_torch, 5)},
         # p10 / p90 of the per-round averages behind each median
