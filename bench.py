@@ -670,7 +670,6 @@ def main():
     torch.cuda.synchronize()
     # the headline: K consecutive steps after W warm-up steps
     ms = time_region(step, args.steps, args.warmup, stream)
-
     # comparisons: the sparse layer, the dense layer, the split of the sparse
     # layer and hipBLASLt take turns, so each sees the same clock and power
     # state (a sustained matrix-core load lowers the clock within milliseconds)
