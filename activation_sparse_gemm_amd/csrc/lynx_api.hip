@@ -2,8 +2,10 @@
 // The operations themselves are defined in lynx.h; the kernels live in the
 // other translation units.
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 
+#include "lynx_debug.h"
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -113,6 +115,23 @@ size_t sparse_workspace_bytes(int64_t M, int64_t K, int64_t R) {
     return layout_for(M, K, R).total;
 }
 
+lynx_status debug_sync(lynx_status st, hipStream_t stream) {
+    if (st != LYNX_OK) return st;
+    const char* v = std::getenv("LYNX_DEBUG");
+    if (!v || !*v || std::strcmp(v, "0") == 0) return st;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return LYNX_ERR_DEVICE;
+    }
+    if (cs != hipStreamCaptureStatusNone) return st;
+    if (hipStreamSynchronize(stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return LYNX_ERR_DEVICE;
+    }
+    return st;
+}
+
 // the sparse layer on validated arguments
 lynx_status run_sparse_layer(const uint16_t* X, const uint16_t* W, const uint16_t* LA,
                              const uint16_t* LB, uint16_t* Y, int64_t M, int64_t N, int64_t K,
@@ -172,8 +191,10 @@ lynx_status lynx_sparsify(const uint16_t* X, const uint16_t* LB, int64_t M, int6
     if (R > 0 && (!aligned16(LB) || !aligned16(T))) return LYNX_ERR_ALIGN;
     lynx_status st = check_device();
     if (st != LYNX_OK) return st;
-    return launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values, meta, scale,
-                           R > 0 ? T : nullptr, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return debug_sync(launch_sparsify(X, R > 0 ? LB : nullptr, int(M), int(K), int(R), values,
+                                      meta, scale, R > 0 ? T : nullptr, s),
+                      s);
 }
 
 lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t* meta,
@@ -191,9 +212,10 @@ lynx_status lynx_linear_sparse_lora_packed(const uint16_t* values, const uint8_t
     if (R > 0 && (!aligned16(T) || !aligned16(LA))) return LYNX_ERR_ALIGN;
     lynx_status st = check_device();
     if (st != LYNX_OK) return st;
-    return launch_gemm_sparse(values, meta, scale, R > 0 ? T : nullptr, W, R > 0 ? LA : nullptr,
-                              Y, int(M), int(N), int(K), int(R),
-                              static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return debug_sync(launch_gemm_sparse(values, meta, scale, R > 0 ? T : nullptr, W,
+                                         R > 0 ? LA : nullptr, Y, int(M), int(N), int(K), int(R), s),
+                      s);
 }
 
 
@@ -235,8 +257,8 @@ lynx_status lynx_linear_sparse_lora(const uint16_t* X, const uint16_t* W, const 
     if (st != LYNX_OK || noop) return st;
     st = check_device();
     if (st != LYNX_OK) return st;
-    return run_sparse_layer(X, W, LA, LB, Y, M, N, K, R, workspace,
-                            static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return debug_sync(run_sparse_layer(X, W, LA, LB, Y, M, N, K, R, workspace, s), s);
 }
 
 lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y, int64_t M,
@@ -246,7 +268,8 @@ lynx_status lynx_linear_dense(const uint16_t* X, const uint16_t* W, uint16_t* Y,
     if (st != LYNX_OK || noop) return st;
     st = check_device();
     if (st != LYNX_OK) return st;
-    return launch_gemm_dense(X, W, Y, int(M), int(N), int(K), static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return debug_sync(launch_gemm_dense(X, W, Y, int(M), int(N), int(K), s), s);
 }
 
 size_t lynx_sequence_workspace_bytes(const lynx_layer* layers, int64_t n) {
@@ -304,7 +327,7 @@ lynx_status lynx_linear_sequence(const lynx_layer* layers, int64_t n, void* work
         }
         if (st != LYNX_OK) return st;
     }
-    return LYNX_OK;
+    return debug_sync(LYNX_OK, s);
 }
 
 }  // extern "C"

@@ -5,6 +5,7 @@
 #include <atomic>
 #include <mutex>
 
+#include "lynx_debug.h"
 #include "lynx_internal.h"
 
 namespace lynx {
@@ -66,5 +67,6 @@ extern "C" lynx_status lynx_linear_sparse_lora_noalloc(const uint16_t* X, const 
     char* ws = nullptr;
     st = scratch_of_current_device(&ws);
     if (st != LYNX_OK) return st;
-    return run_sparse_layer(X, W, LA, LB, Y, M, N, K, R, ws, static_cast<hipStream_t>(stream));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    return debug_sync(run_sparse_layer(X, W, LA, LB, Y, M, N, K, R, ws, s), s);
 }

@@ -23,12 +23,19 @@
  *     stored as described below; every pointer must be 16-byte aligned.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
  *     stream).  The library never allocates device memory, never synchronizes
- *     and keeps no per-call state, so calls are re-entrant; concurrent calls
- *     that write the same buffers race, as with any kernel.
+ *     (outside the debug mode below) and keeps no per-call state, so calls are
+ *     re-entrant; concurrent calls that write the same buffers race, as with
+ *     any kernel.
  *   - All arguments are validated before anything is launched.  On an error
  *     the status is returned and no output is written.
  *   - Asynchronous device faults surface at the caller's next synchronization
  *     with the stream, not as a status of the call that queued the work.
+ *   - Debug mode: with the environment variable LYNX_DEBUG set to anything but
+ *     "" or "0" (read on every call), a call that queued work waits for
+ *     `stream` before it returns, and a failure of that wait (a fault of this
+ *     call's kernels or of earlier work on the stream) is returned as
+ *     LYNX_ERR_DEVICE.  A stream that is being captured into a graph is not
+ *     waited for.  It serializes the caller; it is meant for debugging.
  *   - Inputs must be finite; NaN/Inf inputs give unspecified outputs.
  *   - Shape limits: K is a positive multiple of 64; M >= 0 and N >= 0 (0 is a
  *     no-op); R (LoRA rank) is one of 0, 16, 32, 48, 64 (0 = no LoRA branch);

@@ -226,6 +226,20 @@ def test_valid_arguments_without_gpu_report_unsupported_device():
     assert call_linear() == UNSUPPORTED
 
 
+@pytest.mark.parametrize("value", ["1", "0", ""])
+def test_debug_mode_leaves_validation_unchanged(monkeypatch, value):
+    """LYNX_DEBUG only adds a wait after work was queued: every argument error,
+    every no-op and the device check come out as without it."""
+    monkeypatch.setenv("LYNX_DEBUG", value)
+    assert call_sparsify(K=100) == SHAPE and call_sparsify(X=None) == NULL
+    assert call_sparsify(M=0) == OK
+    assert call_linear(wsb=100) == WORKSPACE and call_linear(N=0) == OK
+    assert _abi.lib().lynx_linear_sequence(None, 0, B, 1 << 20, None) == OK
+    import torch
+    if not torch.cuda.is_available():
+        assert call_sparsify() == UNSUPPORTED and call_linear() == UNSUPPORTED
+
+
 def test_binding_raises_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "_lib", None)
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
