@@ -74,6 +74,9 @@ def parse():
                    help="time the fused-sparsifier GEMM prototype (tests/proto) against the "
                         "library's sparsifier + sparse GEMM pair on the MLP-up, MLP-down and QKV "
                         "shapes (interleaved, --rounds x --calls) and exit")
+    p.add_argument("--report", nargs="+", metavar="JSON",
+                   help="no GPU: render the JSON lines of earlier runs of this benchmark (one or "
+                        "more files) as one Markdown table and exit")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="no GPU: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of a "
                         "--copy-calibration run into profiles/traffic_<workload>.json")
@@ -560,8 +563,86 @@ def fusion_prototype(rounds: int, calls: int, nsets: int) -> dict:
     return {"ms": out, "rounds": rounds, "calls": calls, "sets": nsets}
 
 
+REPORT_COLUMNS = (
+    ("workload", None), ("TFLOP/s (steps)", None), ("ms/step", None),
+    ("sparse layer µs", None), ("dense (K3) µs", None), ("hipBLASLt µs", None),
+    ("vs K3", None), ("vs hipBLASLt", None), ("vs best dense", None),
+    ("K1 µs", None), ("K2 µs", None), ("K2 roofline", None), ("K2 MFMA busy", None),
+    ("K1 HBM frac", None), ("CPU oracle TFLOP/s", None))
+
+
+REPORT_HEAD = """# Benchmark report: RT-Lynx sparse + LoRA linear on one MI355X
+
+Rendered by `python bench.py --report` from the JSON lines that `python bench.py` (MLP-up, with the CPU
+baseline) and `python bench.py --workload W --steps 30 --warmup 5 --no-cpu` (the other workloads) printed:
+{files}.
+"""
+
+REPORT_LEGEND = """Columns:
+- **TFLOP/s (steps), ms/step**: the benchmark's `value` and `ms_per_step`, dense-equivalent flops
+  (2·M·N·K plus the LoRA flops) over consecutive steps.
+- **sparse layer, dense (K3), hipBLASLt**: interleaved medians of the sparse + LoRA layer, the library's dense
+  bf16 layer and `torch.matmul`.
+- **vs K3, vs hipBLASLt, vs best dense**: their ratios to the sparse layer; the last is against the faster of
+  the two dense layers.
+- **K1, K2**: the sparsifier and the sparse GEMM with its LoRA epilogue, timed on their own.
+- **K2 roofline**: K2's flops per second over the dense bf16 peak ({peak_mfma} TFLOP/s).
+- **K2 MFMA busy**: matrix-core busy fraction from the committed rocprofv3 counters (a dash where none were
+  taken).
+- **K1 HBM frac**: K1's algorithmic bytes per second over {peak_hbm:.0f} GB/s.
+- **CPU oracle**: the fp64 oracle on the host cores, on a bounded sample.
+"""
+
+
+def render_report(records: list) -> str:
+    """One Markdown table row per benchmark record (the JSON line main() prints)."""
+    def us(ms):
+        return "—" if ms is None else f"{ms * 1e3:.1f}"
+
+    def x(v):
+        return "—" if v is None else f"{v:.2f}×"
+
+    lines = ["| " + " | ".join(c for c, _ in REPORT_COLUMNS) + " |",
+             "|" + "---|" * len(REPORT_COLUMNS)]
+    for r in records:
+        inter, split = r.get("interleaved_ms", {}), r.get("split_ms", {})
+        busy = r.get("mfma_busy") or {}
+        k2_busy = next((v for k, v in busy.items() if k.startswith("gemm_sparse32")), None)
+        cpu = r.get("cpu_baseline")
+        roof, k1roof = r.get("roofline") or {}, r.get("sparsify_roofline") or {}
+        cells = [r["config"]["workload"].split(":")[0], f"{r['value']:.0f}", f"{r['ms_per_step']:.4f}",
+                 us(inter.get("sparse_layer")), us(inter.get("dense_layer")), us(inter.get("torch_matmul")),
+                 x(r.get("speedup_vs_dense")), x(r.get("speedup_vs_torch_matmul")),
+                 x(r.get("speedup_vs_best_dense")), us(split.get("sparsify")),
+                 us(split.get("sparse_gemm_lora")),
+                 "—" if roof.get("frac") is None else f"{roof['frac']:.3f}",
+                 "—" if k2_busy is None else f"{k2_busy:.2f}",
+                 "—" if k1roof.get("frac") is None else f"{k1roof['frac']:.3f}",
+                 "—" if cpu is None else f"{cpu['value']:.3f} ({cpu['cores']} threads)"]
+        lines.append("| " + " | ".join(cells) + " |")
+    return "\n".join(lines) + "\n"
+
+
+def read_records(paths: list) -> list:
+    """The last JSON line with a "metric" key of each file."""
+    out = []
+    for path in paths:
+        with open(path) as f:
+            recs = [json.loads(t) for t in f.read().splitlines() if t.startswith("{")]
+        recs = [r for r in recs if "metric" in r]
+        if not recs:
+            raise SystemExit(f"{path}: no benchmark record")
+        out.append(recs[-1])
+    return out
+
+
 def main():
     args = parse()
+    if args.report:
+        print(REPORT_HEAD.format(files=", ".join(f"`{os.path.basename(f)}`" for f in args.report)))
+        print(render_report(read_records(args.report)))
+        print(REPORT_LEGEND.format(peak_mfma=PEAK_DENSE_BF16_TFLOPS, peak_hbm=PEAK_HBM_GBS), end="")
+        return
     if args.mfma_peak:
         print(json.dumps(mfma_peak()))
         return
