@@ -11,12 +11,15 @@ MLP-down) in sequence.  Inputs rotate over three independent sets
 (X, W, LA, LB, Y, workspace) so the working set (> 600 MB) exceeds the 256 MB
 last-level cache.
 
-Then the sparse layer, the dense bf16 MFMA layer (lynx_linear_dense, the
+First the sparse layer, the dense bf16 MFMA layer (lynx_linear_dense, the
 speedup baseline), the sparsifier alone and the GEMM alone (split of the sparse
 layer's time) and torch.matmul (hipBLASLt, a reference the library never calls)
 take turns in rounds of --calls calls; each reports the median over --rounds
-rounds, so all of them are timed under the same clock and power state.  The CPU oracle is timed on a bounded sample on the
-host (cpu_baseline).  Prints ONE JSON line.
+rounds, so all of them are timed under the same clock and power state.  Then
+the headline: --warmup untimed steps and --steps timed steps, back to back,
+while the clock is settled from that load; the same steps started after half a
+second of idle are reported beside it (ms_per_step_after_idle).  The CPU oracle
+is timed on a bounded sample on the host (cpu_baseline).  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -74,6 +77,9 @@ def parse():
                    help="time the fused-sparsifier GEMM prototype (tests/proto) against the "
                         "library's sparsifier + sparse GEMM pair on the MLP-up, MLP-down and QKV "
                         "shapes (interleaved, --rounds x --calls) and exit")
+    p.add_argument("--sustained", type=float, metavar="SECONDS",
+                   help="after 1 s of idle, run the workload's step back to back for SECONDS and "
+                        "print the time per step over elapsed time (one JSON line) and exit")
     p.add_argument("--report", nargs="+", metavar="JSON",
                    help="no GPU: render the JSON lines of earlier runs of this benchmark (one or "
                         "more files) as one Markdown table and exit")
@@ -122,6 +128,36 @@ def time_interleaved(fns: dict, rounds: int, calls: int, stream) -> dict:
         v = sorted(v)
         return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
     return {name: (statistics.median(v), pct(v, 0.1), pct(v, 0.9)) for name, v in per.items()}
+
+
+SUSTAINED_MARKS_MS = (1, 2, 5, 10, 20, 50, 100, 200, 500, 1000, 2000, 5000, 10000, 20000, 60000)
+
+
+def sustained(step, seconds: float, stream, chunk: int = 10, idle_s: float = 1.0) -> dict:
+    """Time per step over `seconds` of back-to-back steps that start after
+    `idle_s` of idle: one value per chunk of `chunk` steps (HIP events on
+    `stream`), reported at log-spaced elapsed times, and the mean of the run."""
+    import torch
+    torch.cuda.synchronize()
+    time.sleep(idle_s)
+    series, elapsed, i, nxt = [], 0.0, 0, 0
+    while elapsed < seconds * 1e3:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        evs[0].record(stream)
+        for b in range(20):
+            for _ in range(chunk):
+                step(i)
+                i += 1
+            evs[b + 1].record(stream)
+        torch.cuda.synchronize()
+        for b in range(20):
+            per = evs[b].elapsed_time(evs[b + 1]) / chunk
+            elapsed += per * chunk
+            while nxt < len(SUSTAINED_MARKS_MS) and elapsed >= SUSTAINED_MARKS_MS[nxt]:
+                series.append({"elapsed_ms": round(elapsed, 1), "us_per_step": round(per * 1e3, 1)})
+                nxt += 1
+    return {"steps": i, "seconds": round(elapsed / 1e3, 3), "idle_s_before": idle_s,
+            "chunk_steps": chunk, "mean_us_per_step": round(elapsed / i * 1e3, 2), "series": series}
 
 
 def cpu_model() -> str:
@@ -248,6 +284,7 @@ KERNEL_SOURCES = {
     "sparsify_kernel": ("k_sparsify.hip", "lynx_internal.h"),
 }
 COPY_MIB = 256
+IDLE_S = 0.5   # idle before the from-idle repeat of the headline steps
 
 
 def source_sha(kernel: str) -> str:
@@ -749,14 +786,25 @@ def main():
             torch.matmul(d["X"], d["W"].t(), out=d["Yd"])
 
     torch.cuda.synchronize()
-    # the headline: K consecutive steps after W warm-up steps
-    ms = time_region(step, args.steps, args.warmup, stream)
+    if args.sustained:
+        print(json.dumps(dict(sustained(step, args.sustained, stream), workload=args.workload)))
+        return
     # comparisons: the sparse layer, the dense layer, the split of the sparse
     # layer and hipBLASLt take turns, so each sees the same clock and power
-    # state (a sustained matrix-core load lowers the clock within milliseconds)
+    # state
     med = time_interleaved({"sparse": step, "dense": dense, "gemm": gemm_only,
                             "sparsify": sparsify_only, "torch": torch_mm},
                            rounds=args.rounds, calls=args.calls, stream=stream)
+    # the headline: K consecutive steps after W warm-up steps, right after the
+    # comparisons.  Coming out of idle (input set-up), the first ~20 ms of
+    # back-to-back steps run through a power-management transient, up to 25%
+    # slower than the rate the chip then holds for seconds (--sustained); after
+    # the comparisons' GPU load the clock has settled.  The same W + K steps
+    # started after IDLE_S of idle are reported beside it.
+    ms = time_region(step, args.steps, args.warmup, stream)
+    torch.cuda.synchronize()
+    time.sleep(IDLE_S)
+    ms_idle = time_region(step, args.steps, args.warmup, stream)
     ms_sparse_i, ms_dense = med["sparse"][0], med["dense"][0]
     ms_gemm, ms_k1, ms_torch = med["gemm"][0], med["sparsify"][0], med["torch"][0]
 
@@ -804,6 +852,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_per_step_after_idle": round(ms_idle, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
