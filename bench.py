@@ -601,7 +601,7 @@ def fusion_prototype(rounds: int, calls: int, nsets: int) -> dict:
 
 
 REPORT_COLUMNS = (
-    ("workload", None), ("TFLOP/s (steps)", None), ("ms/step", None),
+    ("workload", None), ("TFLOP/s (steps)", None), ("ms/step", None), ("ms/step after idle", None),
     ("sparse layer µs", None), ("dense (K3) µs", None), ("hipBLASLt µs", None),
     ("vs K3", None), ("vs hipBLASLt", None), ("vs best dense", None),
     ("K1 µs", None), ("K2 µs", None), ("K2 roofline", None), ("K2 MFMA busy", None),
@@ -617,7 +617,8 @@ baseline) and `python bench.py --workload W --steps 30 --warmup 5 --no-cpu` (the
 
 REPORT_LEGEND = """Columns:
 - **TFLOP/s (steps), ms/step**: the benchmark's `value` and `ms_per_step`, dense-equivalent flops
-  (2·M·N·K plus the LoRA flops) over consecutive steps.
+  (2·M·N·K plus the LoRA flops) over consecutive steps at the settled clock; **after idle**: the same steps
+  started after half a second of idle (the clock's transient).
 - **sparse layer, dense (K3), hipBLASLt**: interleaved medians of the sparse + LoRA layer, the library's dense
   bf16 layer and `torch.matmul`.
 - **vs K3, vs hipBLASLt, vs best dense**: their ratios to the sparse layer; the last is against the faster of
@@ -647,7 +648,9 @@ def render_report(records: list) -> str:
         k2_busy = next((v for k, v in busy.items() if k.startswith("gemm_sparse32")), None)
         cpu = r.get("cpu_baseline")
         roof, k1roof = r.get("roofline") or {}, r.get("sparsify_roofline") or {}
+        idle = r.get("ms_per_step_after_idle")
         cells = [r["config"]["workload"].split(":")[0], f"{r['value']:.0f}", f"{r['ms_per_step']:.4f}",
+                 "—" if idle is None else f"{idle:.4f}",
                  us(inter.get("sparse_layer")), us(inter.get("dense_layer")), us(inter.get("torch_matmul")),
                  x(r.get("speedup_vs_dense")), x(r.get("speedup_vs_torch_matmul")),
                  x(r.get("speedup_vs_best_dense")), us(split.get("sparsify")),

@@ -126,7 +126,7 @@ def test_source_hash_covers_the_kernel_headers(monkeypatch, tmp_path):
 def test_report_renders_one_row_per_record(tmp_path):
     """--report: the last benchmark line of each file becomes one table row,
     times in µs, ratios with two decimals, missing counters as a dash."""
-    rec = {"metric": "m", "value": 1456.2, "ms_per_step": 0.218,
+    rec = {"metric": "m", "value": 1456.2, "ms_per_step": 0.218, "ms_per_step_after_idle": 0.23,
            "config": {"workload": "mlp_up: X[4096x3072] -> Y[4096x12288]"},
            "interleaved_ms": {"sparse_layer": 0.19026, "dense_layer": 0.27192, "torch_matmul": 0.22773},
            "split_ms": {"sparsify": 0.01745, "sparse_gemm_lora": 0.17202},
@@ -135,16 +135,17 @@ def test_report_renders_one_row_per_record(tmp_path):
            "mfma_busy": {"gemm_dense32<4>": 0.716, "gemm_sparse32<4>": 0.5996},
            "cpu_baseline": {"value": 0.2371, "cores": 16}}
     other = dict(rec, config={"workload": "tiny: ..."}, mfma_busy=None, cpu_baseline=None)
+    del other["ms_per_step_after_idle"]
     a, b = tmp_path / "a.json", tmp_path / "b.json"
     a.write_text("warm-up noise\n" + json.dumps(dict(rec, value=1.0)) + "\n" + json.dumps(rec) + "\n")
     b.write_text(json.dumps(other) + "\n")
     table = bench.render_report(bench.read_records([str(a), str(b)])).splitlines()
     assert len(table) == 4 and table[1].count("---") == len(bench.REPORT_COLUMNS)
     row = [c.strip() for c in table[2].strip("|").split("|")]
-    assert row == ["mlp_up", "1456", "0.2180", "190.3", "271.9", "227.7", "1.43×", "1.20×", "1.20×",
+    assert row == ["mlp_up", "1456", "0.2180", "0.2300", "190.3", "271.9", "227.7", "1.43×", "1.20×", "1.20×",
                    "17.4", "172.0", "0.372", "0.60", "0.288", "0.237 (16 threads)"]
     tiny = [c.strip() for c in table[3].strip("|").split("|")]
-    assert tiny[0] == "tiny" and tiny[12] == "—" and tiny[14] == "—"
+    assert tiny[0] == "tiny" and tiny[13] == "—" and tiny[15] == "—"
     (tmp_path / "none.json").write_text("no record\n")
     with pytest.raises(SystemExit):
         bench.read_records([str(a), str(tmp_path / "none.json")])
