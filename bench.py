@@ -404,9 +404,9 @@ def summarize_mfma(sq_dir: str, workload: str) -> dict:
     return rec
 
 
-TRACE_CALLS = ("over every call bench.py makes: the consecutive timed steps, then the "
-               "interleaved rounds of the sparse layer, the dense layer, the GEMM alone, the "
-               "sparsifier alone and torch.matmul (hipBLASLt).")
+TRACE_CALLS = ("over every call bench.py makes: the interleaved rounds of the sparse layer, the "
+               "dense layer, the GEMM alone, the sparsifier alone and torch.matmul (hipBLASLt), "
+               "then the consecutive timed steps, then the same steps after half a second of idle.")
 FUSION_CALLS = ("over every call bench.py --fusion-prototype makes: per shape (MLP-up, "
                 "MLP-down, QKV), interleaved rounds of the library's layer (sparsifier + "
                 "sparse GEMM with the rank-64 LoRA), the sparsifier alone, the sparse GEMM alone "
