@@ -119,10 +119,12 @@ lynx_status debug_sync(lynx_status st, hipStream_t stream) {
     if (st != LYNX_OK) return st;
     const char* v = std::getenv("LYNX_DEBUG");
     if (!v || !*v || std::strcmp(v, "0") == 0) return st;
+    // no wait on a stream under capture, nor when the query itself fails (as
+    // it can for the legacy stream while another stream captures globally)
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
         (void)hipGetLastError();
-        return LYNX_ERR_DEVICE;
+        return st;
     }
     if (cs != hipStreamCaptureStatusNone) return st;
     if (hipStreamSynchronize(stream) != hipSuccess) {

@@ -12,7 +12,8 @@ namespace lynx {
 // anything but "" or "0" (read on every call).  Then it waits for `stream`
 // and returns LYNX_ERR_DEVICE if the wait reports an error (a kernel fault
 // of this call or of earlier work on the stream).  A stream that is being
-// captured into a graph is not waited for.
+// captured into a graph, or whose capture state cannot be queried, is not
+// waited for.
 lynx_status debug_sync(lynx_status st, hipStream_t stream);
 
 }  // namespace lynx
