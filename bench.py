@@ -79,7 +79,11 @@ def parse():
                         "shapes (interleaved, --rounds x --calls) and exit")
     p.add_argument("--sustained", type=float, metavar="SECONDS",
                    help="after 1 s of idle, run the workload's step back to back for SECONDS and "
-                        "print the time per step over elapsed time (one JSON line) and exit")
+                        "print the time per step over elapsed time, with the board power sampled "
+                        "meanwhile (one JSON line) and exit")
+    p.add_argument("--sustained-op", choices=("layer", "dense", "torch"), default="layer",
+                   help="with --sustained: the sparse + LoRA layer (default), the library's dense "
+                        "layer, or torch.matmul (hipBLASLt)")
     p.add_argument("--report", nargs="+", metavar="JSON",
                    help="no GPU: render the JSON lines of earlier runs of this benchmark (one or "
                         "more files) as one Markdown table and exit")
@@ -133,15 +137,87 @@ def time_interleaved(fns: dict, rounds: int, calls: int, stream) -> dict:
 SUSTAINED_MARKS_MS = (1, 2, 5, 10, 20, 50, 100, 200, 500, 1000, 2000, 5000, 10000, 20000, 60000)
 
 
+class PowerSampler:
+    """Samples the GPU's board power (hwmon power1_input, µW) and, where the
+    driver exposes it, the current shader clock level (pp_dpm_sclk) on a
+    background thread; reads nothing else and writes nothing."""
+
+    def __init__(self, period_s: float = 0.02):
+        import glob
+        self.period = period_s
+        hw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.power_path = hw[0] if hw else None
+        cap = os.path.join(os.path.dirname(hw[0]), "power1_cap") if hw else None
+        self.cap_w = self._read_w(cap) if cap and os.path.exists(cap) else None
+        sclk = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.sclk_path = sclk[0] if sclk else None
+        self.power, self.sclk, self._stop, self._thread = [], [], False, None
+
+    @staticmethod
+    def _read_w(path):
+        try:
+            with open(path) as f:
+                return int(f.read().strip()) / 1e6
+        except (OSError, ValueError):
+            return None
+
+    def _sclk_mhz(self):
+        try:
+            with open(self.sclk_path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        m = re.search(r"(\d+)\s*[Mm]hz", line)
+                        return int(m.group(1)) if m else None
+        except (OSError, TypeError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop:
+            if self.power_path:
+                w = self._read_w(self.power_path)
+                if w is not None:
+                    self.power.append(w)
+            if self.sclk_path:
+                c = self._sclk_mhz()
+                if c is not None:
+                    self.sclk.append(c)
+            time.sleep(self.period)
+
+    def start(self):
+        import threading
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self) -> dict:
+        self._stop = True
+        if self._thread:
+            self._thread.join()
+
+        def summ(v, nd):
+            if not v:
+                return None
+            v = sorted(v)
+            return {"mean": round(sum(v) / len(v), nd), "p10": round(v[len(v) // 10], nd),
+                    "p90": round(v[(9 * len(v)) // 10], nd), "samples": len(v)}
+        return {"power_w": summ(self.power, 1), "power_cap_w": self.cap_w,
+                "sclk_mhz": summ(self.sclk, 0)}
+
+
 def sustained(step, seconds: float, stream, chunk: int = 10, idle_s: float = 1.0) -> dict:
     """Time per step over `seconds` of back-to-back steps that start after
     `idle_s` of idle: one value per chunk of `chunk` steps (HIP events on
-    `stream`), reported at log-spaced elapsed times, and the mean of the run."""
+    `stream`), reported at log-spaced elapsed times, and the mean of the run;
+    the board power over the second half of the run (PowerSampler)."""
     import torch
     torch.cuda.synchronize()
     time.sleep(idle_s)
+    sampler, sampling = PowerSampler(), False
     series, elapsed, i, nxt = [], 0.0, 0, 0
     while elapsed < seconds * 1e3:
+        if not sampling and elapsed >= seconds * 500:   # the settled second half
+            sampler.start()
+            sampling = True
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
         evs[0].record(stream)
         for b in range(20):
@@ -156,8 +232,10 @@ def sustained(step, seconds: float, stream, chunk: int = 10, idle_s: float = 1.0
             while nxt < len(SUSTAINED_MARKS_MS) and elapsed >= SUSTAINED_MARKS_MS[nxt]:
                 series.append({"elapsed_ms": round(elapsed, 1), "us_per_step": round(per * 1e3, 1)})
                 nxt += 1
+    power = sampler.stop() if sampling else None
     return {"steps": i, "seconds": round(elapsed / 1e3, 3), "idle_s_before": idle_s,
-            "chunk_steps": chunk, "mean_us_per_step": round(elapsed / i * 1e3, 2), "series": series}
+            "chunk_steps": chunk, "mean_us_per_step": round(elapsed / i * 1e3, 2), "series": series,
+            "second_half": power}
 
 
 def cpu_model() -> str:
@@ -790,7 +868,9 @@ def main():
 
     torch.cuda.synchronize()
     if args.sustained:
-        print(json.dumps(dict(sustained(step, args.sustained, stream), workload=args.workload)))
+        fn = {"layer": step, "dense": dense, "torch": torch_mm}[args.sustained_op]
+        print(json.dumps(dict(sustained(fn, args.sustained, stream), workload=args.workload,
+                              op=args.sustained_op)))
         return
     # comparisons: the sparse layer, the dense layer, the split of the sparse
     # layer and hipBLASLt take turns, so each sees the same clock and power

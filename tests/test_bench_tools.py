@@ -149,3 +149,22 @@ def test_report_renders_one_row_per_record(tmp_path):
     (tmp_path / "none.json").write_text("no record\n")
     with pytest.raises(SystemExit):
         bench.read_records([str(a), str(tmp_path / "none.json")])
+
+
+def test_power_sampler_reads_hwmon_and_sclk(tmp_path):
+    """--sustained's sampler: board power from hwmon (µW) and the starred
+    shader-clock level of pp_dpm_sclk; missing files give nulls."""
+    (tmp_path / "power1_input").write_text("750000000\n")
+    (tmp_path / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1500Mhz *\n2: 2400Mhz\n")
+    ps = bench.PowerSampler(period_s=0.001)
+    ps.power_path, ps.sclk_path, ps.cap_w = str(tmp_path / "power1_input"), str(tmp_path / "pp_dpm_sclk"), 1400.0
+    ps.start()
+    import time
+    time.sleep(0.05)
+    out = ps.stop()
+    assert out["power_w"]["mean"] == 750.0 and out["power_w"]["samples"] > 0
+    assert out["sclk_mhz"]["mean"] == 1500 and out["power_cap_w"] == 1400.0
+    empty = bench.PowerSampler()
+    empty.power_path = empty.sclk_path = None
+    empty.start()
+    assert empty.stop()["power_w"] is None
